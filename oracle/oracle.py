@@ -1,0 +1,157 @@
+"""ctypes front end of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in
+__graft_entry__.py and by the cpu_baseline leg of bench.py, never by the
+product package.  It shares no code with the HIP library.
+
+All arrays are NumPy; bf16 values travel as their uint16 bit patterns.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        L = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_double.restype = f64
+        L.oracle_e2m1_value.argtypes = [i32]
+        L.oracle_e2m1_value.restype = f64
+        L.oracle_e8m0_value.argtypes = [i32]
+        L.oracle_e8m0_value.restype = f64
+        L.oracle_scale_exponent.argtypes = [f64, i32]
+        L.oracle_scale_exponent.restype = i32
+        L.oracle_e2m1_encode.argtypes = [f64]
+        L.oracle_e2m1_encode.restype = i32
+        L.oracle_quantize.argtypes = [P, i64, i64, i32, P, P]
+        L.oracle_quantize.restype = i32
+        L.oracle_dequantize.argtypes = [P, P, i64, i64, P]
+        L.oracle_dequantize.restype = None
+        L.oracle_route.argtypes = [P, P, P, i32, i32, i32, i32,
+                                   P, P, P, P, P, P, P, P]
+        L.oracle_route.restype = i32
+        L.oracle_moe.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                 P, i32, P]
+        L.oracle_moe.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# -- scalars ---------------------------------------------------------------
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e8m0_value(byte: int) -> float:
+    return lib().oracle_e8m0_value(int(byte))
+
+
+def scale_exponent(amax: float, rule: int = 0) -> int:
+    return lib().oracle_scale_exponent(float(amax), int(rule))
+
+
+def e2m1_encode(y: float) -> int:
+    return lib().oracle_e2m1_encode(float(y))
+
+
+# -- MXFP4 -----------------------------------------------------------------
+
+def quantize(w_bf16: np.ndarray, rule: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [..., K] -> (packed codes [..., K/2], E8M0 scales [..., K/32])."""
+    w = _c(w_bf16, np.uint16)
+    K = w.shape[-1]
+    rows = w.size // K
+    q = np.empty(w.shape[:-1] + (K // 2,), dtype=np.uint8)
+    s = np.empty(w.shape[:-1] + (K // 32,), dtype=np.uint8)
+    rc = lib().oracle_quantize(_ptr(w), rows, K, rule, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle_quantize rejected its arguments (rc=%d)" % rc)
+    return q, s
+
+
+def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    K = q.shape[-1] * 2
+    rows = q.size // q.shape[-1]
+    out = np.empty(q.shape[:-1] + (K,), dtype=np.float64)
+    lib().oracle_dequantize(_ptr(q), _ptr(s), rows, K, _ptr(out))
+    return out
+
+
+# -- routing ---------------------------------------------------------------
+
+def route(x_bf16: np.ndarray, wr: np.ndarray, b: np.ndarray | None, k: int) -> dict:
+    x = _c(x_bf16, np.uint16)
+    wr = _c(wr, np.float32)
+    T, D = x.shape
+    E = wr.shape[0]
+    bb = None if b is None else _c(b, np.float32)
+    out = dict(
+        logits=np.empty((T, E), np.float64), ids=np.empty((T, k), np.int32),
+        w=np.empty((T, k), np.float64), gap=np.empty(T, np.float64),
+        counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
+        sorted=np.empty(T * k, np.int32), pos=np.empty(T * k, np.int32))
+    rc = lib().oracle_route(_ptr(x), _ptr(wr), _ptr(bb), T, D, E, k,
+                            _ptr(out["logits"]), _ptr(out["ids"]), _ptr(out["w"]),
+                            _ptr(out["gap"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+                            _ptr(out["sorted"]), _ptr(out["pos"]))
+    if rc != 0:
+        raise ValueError("oracle_route rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+# -- expert MLP + combine ----------------------------------------------------
+
+def moe(x_bf16, q13, s13, q2, s2, ids, w, F: int, tokens=None) -> np.ndarray:
+    """fp64 layer output for the listed tokens (all tokens if None): [n, D]."""
+    x = _c(x_bf16, np.uint16)
+    T, D = x.shape
+    q13, s13, q2, s2 = (_c(a, np.uint8) for a in (q13, s13, q2, s2))
+    E = q13.shape[0]
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float64)
+    k = ids.shape[1]
+    toks = None if tokens is None else _c(tokens, np.int32)
+    n = T if toks is None else len(toks)
+    out = np.empty((n, D), np.float64)
+    rc = lib().oracle_moe(_ptr(x), _ptr(q13), _ptr(s13), _ptr(q2), _ptr(s2),
+                          _ptr(ids), _ptr(w), T, D, F, E, k, _ptr(toks), n, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_moe failed (rc=%d)" % rc)
+    return out
