@@ -1,0 +1,246 @@
+"""Thin Python binding of libmoe_mxfp4 (MXFP4 mixture-of-experts MLP layer
+for AMD MI355X / gfx950).
+
+Every step of the layer runs in the HIP kernels of libmoe_mxfp4.so; this
+module only marshals torch tensors (device memory and the current stream)
+into the C ABI declared in include/moe_mxfp4.h.  There is no CPU fallback: if
+the library is missing, or a tensor is not on the GPU, the call raises.
+
+Functions mirror the C entry points:
+    mxfp4_quantize(w, rule)           -> (q, s)
+    mxfp4_dequantize(q, s)            -> bf16 tensor
+    moe_route(x, wr, br, k)           -> Routing
+    moe_expert_mlp(x, weights, routing) -> bf16 [T, D]
+and MoELayer bundles quantized weights and workspaces for repeated calls.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = ["mxfp4_quantize", "mxfp4_dequantize", "moe_route", "moe_expert_mlp",
+           "Routing", "ExpertWeights", "MoELayer", "MoEError", "lib",
+           "SCALE_FLOOR_DIV6", "SCALE_OCP", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
+SCALE_FLOOR_DIV6 = 0
+SCALE_OCP = 1
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().moe_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_mxfp4.so (built in-tree by build.py); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m mxfp4_quantized_mixture_amd.build` "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_abi_version.argtypes = []
+        L.moe_abi_version.restype = ctypes.c_int
+        L.mxfp4_quantize.argtypes = [P, i64, i64, ctypes.c_int, P, P, P]
+        L.mxfp4_quantize.restype = ctypes.c_int
+        L.mxfp4_dequantize.argtypes = [P, P, i64, i64, P, P]
+        L.mxfp4_dequantize.restype = ctypes.c_int
+        L.moe_route_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.moe_route_workspace_size.restype = sz
+        L.moe_route.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_expert_mlp_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_expert_mlp_workspace_size.restype = sz
+        L.moe_expert_mlp.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                     P, P, sz, P, P]
+        L.moe_expert_mlp.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+# ---------------------------------------------------------------- codec
+
+def mxfp4_quantize(w: torch.Tensor, rule: int = SCALE_FLOOR_DIV6):
+    """bf16 [..., K] -> (codes uint8 [..., K/2], E8M0 scales uint8 [..., K/32])."""
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    q = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
+    s = torch.empty(*w.shape[:-1], K // 32, dtype=torch.uint8, device=w.device)
+    _check("mxfp4_quantize", lib().mxfp4_quantize(
+        _dev(w, "w", torch.bfloat16), rows, K, rule, _dev(q, "q"), _dev(s, "s"),
+        _stream(w.device)))
+    return q, s
+
+
+def mxfp4_dequantize(q: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    K = q.shape[-1] * 2
+    rows = q.numel() // q.shape[-1]
+    out = torch.empty(*q.shape[:-1], K, dtype=torch.bfloat16, device=q.device)
+    _check("mxfp4_dequantize", lib().mxfp4_dequantize(
+        _dev(q, "q", torch.uint8), _dev(s, "s", torch.uint8), rows, K, _dev(out, "out"),
+        _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------- routing
+
+@dataclass
+class Routing:
+    ids: torch.Tensor        # int32 [T, k]
+    weights: torch.Tensor    # fp32 [T, k]
+    counts: torch.Tensor     # int32 [E]
+    offsets: torch.Tensor    # int32 [E+1]
+    sorted_pairs: torch.Tensor  # int32 [T*k]
+    pair_pos: torch.Tensor   # int32 [T*k]
+    logits: torch.Tensor | None = None  # fp32 [T, E]
+
+
+def alloc_routing(T: int, E: int, k: int, device, with_logits: bool = False) -> Routing:
+    i32 = dict(dtype=torch.int32, device=device)
+    return Routing(
+        ids=torch.empty(T, k, **i32), weights=torch.empty(T, k, dtype=torch.float32, device=device),
+        counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+        sorted_pairs=torch.empty(T * k, **i32), pair_pos=torch.empty(T * k, **i32),
+        logits=torch.empty(T, E, dtype=torch.float32, device=device) if with_logits else None)
+
+
+def route_workspace(T: int, D: int, E: int, k: int, device) -> torch.Tensor:
+    n = lib().moe_route_workspace_size(T, D, E, k)
+    if n == 0:
+        raise MoEError("moe_route_workspace_size", 2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_route(x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None, k: int,
+              out: Routing | None = None, ws: torch.Tensor | None = None,
+              with_logits: bool = False) -> Routing:
+    T, D = x.shape
+    E = wr.shape[0]
+    if wr.shape[1] != D:
+        raise ValueError("router weight must be [E, D]")
+    r = out if out is not None else alloc_routing(T, E, k, x.device, with_logits)
+    ws = ws if ws is not None else route_workspace(T, D, E, k, x.device)
+    _check("moe_route", lib().moe_route(
+        _dev(x, "x", torch.bfloat16), _dev(wr, "wr", torch.float32),
+        None if br is None else _dev(br, "br", torch.float32), T, D, E, k,
+        _dev(r.ids, "ids"), _dev(r.weights, "weights"), _dev(r.counts, "counts"),
+        _dev(r.offsets, "offsets"), _dev(r.sorted_pairs, "sorted_pairs"),
+        _dev(r.pair_pos, "pair_pos"), None if r.logits is None else _dev(r.logits, "logits"),
+        _dev(ws, "ws"), ws.numel(), _stream(x.device)))
+    return r
+
+
+# ---------------------------------------------------------------- experts
+
+@dataclass
+class ExpertWeights:
+    w13_q: torch.Tensor   # uint8 [E, 2F, D/2]
+    w13_s: torch.Tensor   # uint8 [E, 2F, D/32]
+    w2_q: torch.Tensor    # uint8 [E, D, F/2]
+    w2_s: torch.Tensor    # uint8 [E, D, F/32]
+
+    @property
+    def E(self) -> int:
+        return self.w13_q.shape[0]
+
+    @property
+    def F(self) -> int:
+        return self.w2_q.shape[2] * 2
+
+    @property
+    def D(self) -> int:
+        return self.w2_q.shape[1]
+
+    @classmethod
+    def quantize(cls, w13: torch.Tensor, w2: torch.Tensor, rule: int = SCALE_FLOOR_DIV6):
+        """bf16 W13 [E, 2F, D] and W2 [E, D, F] -> MXFP4."""
+        a, b = mxfp4_quantize(w13, rule)
+        c, d = mxfp4_quantize(w2, rule)
+        return cls(a, b, c, d)
+
+
+def mlp_workspace(T: int, D: int, F: int, E: int, k: int, device) -> torch.Tensor:
+    n = lib().moe_expert_mlp_workspace_size(T, D, F, E, k)
+    if n == 0:
+        raise MoEError("moe_expert_mlp_workspace_size", 2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_expert_mlp(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
+                   out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                   events=None) -> torch.Tensor:
+    T, D = x.shape
+    E, F = weights.E, weights.F
+    k = routing.ids.shape[1]
+    if weights.D != D:
+        raise ValueError("expert weights do not match d_model")
+    out = out if out is not None else torch.empty(T, D, dtype=torch.bfloat16, device=x.device)
+    ws = ws if ws is not None else mlp_workspace(T, D, F, E, k, x.device)
+    ev = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events must hold 4 torch.cuda.Event objects")
+        ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    _check("moe_expert_mlp", lib().moe_expert_mlp(
+        _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
+        _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
+        _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w", torch.float32),
+        _dev(routing.offsets, "offsets", torch.int32),
+        _dev(routing.sorted_pairs, "sorted_pairs", torch.int32),
+        _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
+        _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), ev, _stream(x.device)))
+    return out
+
+
+class MoELayer:
+    """Router + MXFP4 experts with preallocated routing buffers and workspaces."""
+
+    def __init__(self, wr: torch.Tensor, br: torch.Tensor | None, weights: ExpertWeights,
+                 k: int, max_tokens: int):
+        self.wr, self.br, self.weights, self.k = wr, br, weights, k
+        self.max_tokens = max_tokens
+        dev = wr.device
+        E, D, F = weights.E, weights.D, weights.F
+        self.routing = alloc_routing(max_tokens, E, k, dev)
+        self.route_ws = route_workspace(max_tokens, D, E, k, dev)
+        self.mlp_ws = mlp_workspace(max_tokens, D, F, E, k, dev)
+
+    def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None, events=None):
+        T = x.shape[0]
+        if T != self.max_tokens:
+            raise ValueError("MoELayer was sized for %d tokens" % self.max_tokens)
+        r = moe_route(x, self.wr, self.br, self.k, out=self.routing, ws=self.route_ws)
+        return moe_expert_mlp(x, self.weights, r, out=out, ws=self.mlp_ws, events=events)

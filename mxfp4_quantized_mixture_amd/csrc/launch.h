@@ -1,0 +1,38 @@
+// launch.h -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule,
+                           uint8_t* q, uint8_t* s, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
+                             uint16_t* out, hipStream_t stream);
+
+struct RoutePlan {
+    int T, D, E, k;
+    int splits;        // D-slices of the router product (partial sums)
+    int chunks;        // token chunks of the top-k / histogram pass
+    size_t off_partial, off_chunk_counts, off_chunk_base, ws_bytes;
+};
+RoutePlan plan_route(int T, int D, int E, int k);
+hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, const float* br,
+                        int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted, int32_t* pos, float* logits_out, void* ws,
+                        hipStream_t stream);
+
+struct MlpPlan {
+    int T, D, F, E, k;
+    size_t off_h, off_y, ws_bytes;
+};
+MlpPlan plan_mlp(int T, int D, int F, int E, int k);
+hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+                      const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
+                      const float* topk_w, const int32_t* offsets, const int32_t* sorted,
+                      const int32_t* pos, uint16_t* out, void* ws, hipEvent_t* events,
+                      hipStream_t stream);
+
+}  // namespace moe

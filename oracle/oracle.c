@@ -122,18 +122,25 @@ int oracle_scale_exponent(double amax, int rule)
     return s;
 }
 
+/* The 8 non-negative E2M1 values, by magnitude code. */
+static void e2m1_grid(double grid[8])
+{
+    for (int c = 0; c < 8; ++c)
+        grid[c] = oracle_e2m1_value(c);
+}
+
 /* Magnitude code (0..7) of the E2M1 value nearest to a >= 0; ties go to the
  * code whose mantissa bit is 0 (round half to even); values beyond 6 take
  * the largest code (saturation, E2M1 has no infinity). */
-static int e2m1_nearest_magnitude(double a)
+static int e2m1_nearest_magnitude(double a, const double grid[8])
 {
-    if (a >= 6.0)
+    if (a >= grid[7])
         return 7;   /* at or beyond the largest value: saturate (checked first,
                        since for huge a the fp64 distances below all round equal) */
     int best = 0;
-    double best_err = fabs(a - oracle_e2m1_value(0));
+    double best_err = fabs(a - grid[0]);
     for (int c = 1; c < 8; ++c) {
-        double err = fabs(a - oracle_e2m1_value(c));
+        double err = fabs(a - grid[c]);
         if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
             best = c;
             best_err = err;
@@ -142,11 +149,18 @@ static int e2m1_nearest_magnitude(double a)
     return best;
 }
 
+static int e2m1_encode_grid(double y, const double grid[8])
+{
+    int sign = signbit(y) ? 1 : 0;
+    return (sign << 3) | e2m1_nearest_magnitude(fabs(y), grid);
+}
+
 /* E2M1 code of an already-scaled value y (sign kept, including -0). */
 int oracle_e2m1_encode(double y)
 {
-    int sign = signbit(y) ? 1 : 0;
-    return (sign << 3) | e2m1_nearest_magnitude(fabs(y));
+    double grid[8];
+    e2m1_grid(grid);
+    return e2m1_encode_grid(y, grid);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -161,6 +175,8 @@ int oracle_quantize(const uint16_t *w, int64_t rows, int64_t K, int rule,
     if (K % 32 != 0 || (rule != 0 && rule != 1))
         return -1;
     int64_t nblk = K / 32;
+    double grid[8];
+    e2m1_grid(grid);
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nblk; ++b) {
             const uint16_t *blk = w + r * K + b * 32;
@@ -172,11 +188,10 @@ int oracle_quantize(const uint16_t *w, int64_t rows, int64_t K, int rule,
             }
             int se = oracle_scale_exponent(amax, rule);
             s[r * nblk + b] = (uint8_t)(se + 127);
+            double inv_scale = ldexp(1.0, -se);   /* 2^-s: products are exact */
             int codes[32];
-            for (int i = 0; i < 32; ++i) {
-                double y = ldexp(oracle_bf16_to_double(blk[i]), -se); /* exact */
-                codes[i] = oracle_e2m1_encode(y);
-            }
+            for (int i = 0; i < 32; ++i)
+                codes[i] = e2m1_encode_grid(oracle_bf16_to_double(blk[i]) * inv_scale, grid);
             uint8_t *qb = q + r * (K / 2) + b * 16;
             for (int i = 0; i < 16; ++i)
                 qb[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
@@ -294,21 +309,63 @@ int oracle_route(const uint16_t *x, const float *wr, const float *b,
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* Computes out[i, :] for the tokens listed in toks[0..ntok) (all T tokens in
- * order when toks is NULL).
+/* One expert applied to a list of tokens:
+ *   y[i, :] = W2 h,  h = silu(Wg x_t) * (Wu x_t),  t = toks[i], i < n.
+ *   x    bf16 [T, D] (only the listed rows are read)
+ *   q13  [2F, D/2], s13 [2F, D/32]: gate rows 0..F-1, up rows F..2F-1
+ *   q2   [D, F/2],  s2  [D, F/32]
+ *   y    fp64 [n, D]
+ * SwiGLU experts: [WELCOME] s.4; weights kept in MXFP4 and widened only for
+ * the arithmetic: [TALK] hardware section, [TRICKS] s.8.  The expert's
+ * weights are widened to fp64 once, then each token is a plain loop. */
+int oracle_expert_mlp(const uint16_t *x, int D, int F, const uint8_t *q13,
+                      const uint8_t *s13, const uint8_t *q2, const uint8_t *s2,
+                      const int32_t *toks, int n, double *y)
+{
+    if (D % 32 != 0 || F % 32 != 0)
+        return -1;
+    double *w13 = (double *)malloc(sizeof(double) * (size_t)2 * F * D);
+    double *w2 = (double *)malloc(sizeof(double) * (size_t)D * F);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)D);
+    double *h = (double *)malloc(sizeof(double) * (size_t)F);
+    if (!w13 || !w2 || !xd || !h) {
+        free(w13); free(w2); free(xd); free(h);
+        return -2;
+    }
+    oracle_dequantize(q13, s13, 2 * F, D, w13);
+    oracle_dequantize(q2, s2, D, F, w2);
+    for (int i = 0; i < n; ++i) {
+        int t = toks[i];
+        for (int d = 0; d < D; ++d)
+            xd[d] = oracle_bf16_to_double(x[(int64_t)t * D + d]);
+        for (int f = 0; f < F; ++f) {
+            double g = 0.0, u = 0.0;
+            for (int d = 0; d < D; ++d) {
+                g += w13[(int64_t)f * D + d] * xd[d];
+                u += w13[(int64_t)(F + f) * D + d] * xd[d];
+            }
+            h[f] = silu(g) * u;
+        }
+        for (int d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int f = 0; f < F; ++f)
+                acc += w2[(int64_t)d * F + f] * h[f];
+            y[(int64_t)i * D + d] = acc;
+        }
+    }
+    free(w13); free(w2); free(xd); free(h);
+    return 0;
+}
+
+/* The whole layer for the tokens listed in toks[0..ntok) (all T tokens in
+ * order when toks is NULL):
  *   x    bf16 [T, D]
- *   q13  [E, 2F, D/2], s13 [E, 2F, D/32]  gate rows 0..F-1, up rows F..2F-1
- *   q2   [E, D, F/2],  s2  [E, D, F/32]
+ *   q13  [E, 2F, D/2], s13 [E, 2F, D/32];  q2 [E, D, F/2], s2 [E, D, F/32]
  *   ids  [T, k], w [T, k] (fp64 routing weights)
  *   out  fp64 [ntok, D]
- * For each routed pair (t, j) with expert e = ids[t, j]:
- *   g = Wg_e x_t, u = Wu_e x_t, h = silu(g) * u, y = W2_e h,
- *   out[t] = sum_j w[t, j] * y(t, j) in slot order.
- * SwiGLU experts, no shared expert: [WELCOME] s.4, [TALK] Q&A;
- * weights kept in MXFP4 and widened only for the arithmetic: [TALK] hardware
- * section, [TRICKS] s.8.
- * Work is done expert by expert (one expert's weights widened to fp64 at a
- * time) only to bound memory; the arithmetic per pair is the plain one. */
+ * out[t] = sum over slots j = 0..k-1, in slot order, of w[t, j] * y(t, j),
+ * y(t, j) = expert ids[t, j] applied to x_t (no shared expert: [TALK] Q&A).
+ * Experts are visited one at a time only to bound memory. */
 int oracle_moe(const uint16_t *x, const uint8_t *q13, const uint8_t *s13,
                const uint8_t *q2, const uint8_t *s2, const int32_t *ids,
                const double *w, int T, int D, int F, int E, int k,
@@ -318,57 +375,38 @@ int oracle_moe(const uint16_t *x, const uint8_t *q13, const uint8_t *s13,
         return -1;
     if (!toks)
         ntok = T;
-    int64_t n13 = (int64_t)2 * F * D, n2 = (int64_t)D * F;
-    double *w13 = (double *)malloc(sizeof(double) * (size_t)n13);
-    double *w2 = (double *)malloc(sizeof(double) * (size_t)n2);
-    double *xd = (double *)malloc(sizeof(double) * (size_t)D);
-    double *h = (double *)malloc(sizeof(double) * (size_t)F);
     double *y = (double *)malloc(sizeof(double) * (size_t)ntok * k * D);
-    if (!w13 || !w2 || !xd || !h || !y) {
-        free(w13); free(w2); free(xd); free(h); free(y);
+    int32_t *list_tok = (int32_t *)malloc(sizeof(int32_t) * (size_t)ntok * k);
+    int32_t *list_slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)ntok * k);
+    double *ye = (double *)malloc(sizeof(double) * (size_t)ntok * k * D);
+    if (!y || !list_tok || !list_slot || !ye) {
+        free(y); free(list_tok); free(list_slot); free(ye);
         return -2;
     }
-
     for (int e = 0; e < E; ++e) {
-        int used = 0;
-        for (int i = 0; i < ntok && !used; ++i) {
-            int t = toks ? toks[i] : i;
-            for (int j = 0; j < k; ++j)
-                if (ids[(int64_t)t * k + j] == e)
-                    used = 1;
-        }
-        if (!used)
-            continue;
-        oracle_dequantize(q13 + (int64_t)e * 2 * F * (D / 2),
-                          s13 + (int64_t)e * 2 * F * (D / 32), 2 * F, D, w13);
-        oracle_dequantize(q2 + (int64_t)e * D * (F / 2),
-                          s2 + (int64_t)e * D * (F / 32), D, F, w2);
+        int n = 0;
         for (int i = 0; i < ntok; ++i) {
             int t = toks ? toks[i] : i;
-            for (int j = 0; j < k; ++j) {
-                if (ids[(int64_t)t * k + j] != e)
-                    continue;
-                for (int d = 0; d < D; ++d)
-                    xd[d] = oracle_bf16_to_double(x[(int64_t)t * D + d]);
-                for (int f = 0; f < F; ++f) {
-                    double g = 0.0, u = 0.0;
-                    for (int d = 0; d < D; ++d) {
-                        g += w13[(int64_t)f * D + d] * xd[d];
-                        u += w13[(int64_t)(F + f) * D + d] * xd[d];
-                    }
-                    h[f] = silu(g) * u;
+            for (int j = 0; j < k; ++j)
+                if (ids[(int64_t)t * k + j] == e) {
+                    list_tok[n] = t;
+                    list_slot[n] = i * k + j;
+                    ++n;
                 }
-                double *yy = y + ((int64_t)i * k + j) * D;
-                for (int d = 0; d < D; ++d) {
-                    double acc = 0.0;
-                    for (int f = 0; f < F; ++f)
-                        acc += w2[(int64_t)d * F + f] * h[f];
-                    yy[d] = acc;
-                }
-            }
         }
+        if (n == 0)
+            continue;
+        int rc = oracle_expert_mlp(x, D, F, q13 + (int64_t)e * 2 * F * (D / 2),
+                                   s13 + (int64_t)e * 2 * F * (D / 32),
+                                   q2 + (int64_t)e * D * (F / 2),
+                                   s2 + (int64_t)e * D * (F / 32), list_tok, n, ye);
+        if (rc != 0) {
+            free(y); free(list_tok); free(list_slot); free(ye);
+            return rc;
+        }
+        for (int r = 0; r < n; ++r)
+            memcpy(y + (int64_t)list_slot[r] * D, ye + (int64_t)r * D, sizeof(double) * (size_t)D);
     }
-
     for (int i = 0; i < ntok; ++i) {
         int t = toks ? toks[i] : i;
         for (int d = 0; d < D; ++d) {
@@ -378,6 +416,6 @@ int oracle_moe(const uint16_t *x, const uint8_t *q13, const uint8_t *s13,
             out[(int64_t)i * D + d] = acc;
         }
     }
-    free(w13); free(w2); free(xd); free(h); free(y);
+    free(y); free(list_tok); free(list_slot); free(ye);
     return 0;
 }

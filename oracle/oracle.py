@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_moe.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                  P, i32, P]
         L.oracle_moe.restype = i32
+        L.oracle_expert_mlp.argtypes = [P, i32, i32, P, P, P, P, P, i32, P]
+        L.oracle_expert_mlp.restype = i32
         _lib = L
     return _lib
 
@@ -154,4 +157,52 @@ def moe(x_bf16, q13, s13, q2, s2, ids, w, F: int, tokens=None) -> np.ndarray:
                           _ptr(ids), _ptr(w), T, D, F, E, k, _ptr(toks), n, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_moe failed (rc=%d)" % rc)
+    return out
+
+
+def expert_mlp(x_bf16, q13e, s13e, q2e, s2e, F: int, tokens) -> np.ndarray:
+    """One expert on the listed tokens: y [n, D] fp64 (see oracle_expert_mlp)."""
+    x = _c(x_bf16, np.uint16)
+    D = x.shape[1]
+    q13e, s13e, q2e, s2e = (_c(a, np.uint8) for a in (q13e, s13e, q2e, s2e))
+    toks = _c(tokens, np.int32)
+    y = np.empty((len(toks), D), np.float64)
+    rc = lib().oracle_expert_mlp(_ptr(x), D, F, _ptr(q13e), _ptr(s13e), _ptr(q2e), _ptr(s2e),
+                                 _ptr(toks), len(toks), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_expert_mlp failed (rc=%d)" % rc)
+    return y
+
+
+def moe_threaded(x_bf16, expert_weights, ids, w, F: int, tokens=None, threads: int = 8):
+    """Same result as moe(), with experts evaluated on parallel threads.
+
+    expert_weights(e) -> (q13e, s13e, q2e, s2e) returns expert e's MXFP4
+    arrays (so experts can be quantized lazily, on the worker threads).  Each
+    worker runs the single-threaded oracle_expert_mlp; the slot-order combine
+    out[t] = sum_j w[t, j] * y(t, j) is then done here in fp64, j ascending.
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    D = np.asarray(x_bf16).shape[1]
+    y = np.zeros((len(toks), k, D), np.float64)
+    jobs = {}
+    for i, t in enumerate(toks):
+        for j in range(k):
+            jobs.setdefault(int(ids[t, j]), []).append((i, j, int(t)))
+
+    def run(e):
+        q13e, s13e, q2e, s2e = expert_weights(e)
+        lst = jobs[e]
+        ye = expert_mlp(x_bf16, q13e, s13e, q2e, s2e, F, [t for _, _, t in lst])
+        for r, (i, j, _) in enumerate(lst):
+            y[i, j] = ye[r]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, sorted(jobs)))
+    w = np.asarray(w, np.float64)
+    out = np.zeros((len(toks), D), np.float64)
+    for j in range(k):
+        out = out + w[toks, j][:, None] * y[:, j, :]
     return out

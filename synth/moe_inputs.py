@@ -26,6 +26,7 @@ Recipe (one generator per stream, NumPy PCG64 seeded with
 
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -125,11 +126,16 @@ def gen_expert(cfg: MoEConfig, seed: int, e: int) -> tuple[np.ndarray, np.ndarra
     return f32_to_bf16_bits(w13), f32_to_bf16_bits(w2)
 
 
-def gen_experts(cfg: MoEConfig, seed: int) -> tuple[np.ndarray, np.ndarray]:
-    """bf16 bits of all experts: W13 [E, 2F, D], W2 [E, D, F]."""
+def gen_experts(cfg: MoEConfig, seed: int, threads: int = 8) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits of all experts: W13 [E, 2F, D], W2 [E, D, F].  Experts are
+    independent streams, so they are drawn on parallel threads (same bits)."""
     w13 = np.empty((cfg.E, 2 * cfg.F, cfg.D), dtype=np.uint16)
     w2 = np.empty((cfg.E, cfg.D, cfg.F), dtype=np.uint16)
-    for e in range(cfg.E):
+
+    def one(e):
         w13[e], w2[e] = gen_expert(cfg, seed, e)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, range(cfg.E)))
     return w13, w2
 

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: codes, scales, expert ids, histogram, offsets and permutations are
+bit-exact (tokens whose oracle logits have a gap under 1e-4 among their
+k+1 largest are excluded from id comparison, and the permutation is then
+checked against the GPU's own ids); layer outputs satisfy
+max|gpu - ref| <= 2^-7 (|ref| + rms(ref)) elementwise.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_quantized_mixture_amd as moe
+from oracle import oracle as O
+from synth import moe_inputs as MI
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+FINITE = np.array([b for b in range(1 << 16) if ((b >> 7) & 0xFF) != 0xFF], np.uint16)
+NEAR_TIE = 1e-4
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def gpu_quantize(w_bits, rule=0):
+    q, s = moe.mxfp4_quantize(G.bf16_dev(w_bits), rule)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+# ------------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_quantize_every_bf16_as_lone_element(rule):
+    w = np.zeros((len(FINITE), 32), np.uint16)
+    w[np.arange(len(FINITE)), np.arange(len(FINITE)) % 32] = FINITE
+    q, s = gpu_quantize(w, rule)
+    rq, rs = O.quantize(w, rule)
+    assert np.array_equal(s, rs)
+    assert np.array_equal(q, rq)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_quantize_every_bf16_under_many_maxima(rule):
+    rows = []
+    for E in (1, 2, 7, 60, 100, 118, 121, 124, 127, 130, 160, 200, 252, 253, 254):
+        for M in (0, 63, 64, 127):
+            mx = np.uint16(E << 7 | M)
+            vals = FINITE[(FINITE & 0x7FFF) <= mx]
+            n = (len(vals) + 30) // 31
+            blk = np.zeros((n, 32), np.uint16)
+            flat = np.zeros(n * 31, np.uint16)
+            flat[:len(vals)] = vals
+            blk[:, 1:] = flat.reshape(n, 31)
+            blk[:, 0] = mx | (np.uint16(0x8000) if M == 63 else np.uint16(0))
+            rows.append(blk)
+    w = np.concatenate(rows)
+    log("blocks: %d" % len(w))
+    q, s = gpu_quantize(w, rule)
+    rq, rs = O.quantize(w, rule)
+    assert np.array_equal(s, rs)
+    assert np.array_equal(q, rq)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_quantize_random_rows_many_blocks(rule):
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((257, 2880)) * np.exp(rng.uniform(-40, 40, (257, 1)))
+    w = MI.f32_to_bf16_bits(v.astype(np.float32))
+    q, s = gpu_quantize(w, rule)
+    rq, rs = O.quantize(w, rule)
+    assert np.array_equal(s, rs) and np.array_equal(q, rq)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gptoss20b_decode", "gptoss120b_decode"])
+def test_quantize_workload_experts(name):
+    cfg = MI.CONFIGS[name]
+    for e in (0, cfg.E - 1):
+        w13, w2 = MI.gen_expert(cfg, 0, e)
+        for w in (w13, w2):
+            q, s = gpu_quantize(w)
+            rq, rs = O.quantize(w)
+            assert np.array_equal(s, rs) and np.array_equal(q, rq)
+    if cfg.outliers:
+        # outlier blocks raise their scale well above the N(0, 0.02) blocks
+        assert rs.max() >= rs.min() + 4
+
+
+def test_dequantize_matches_oracle():
+    rng = np.random.default_rng(22)
+    v = rng.standard_normal((64, 320)) * np.exp(rng.uniform(-20, 20, (64, 1)))
+    w = MI.f32_to_bf16_bits(v.astype(np.float32))
+    q, s = O.quantize(w)
+    out = moe.mxfp4_dequantize(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda())
+    got = G.bf16_bits_to_f64(G.bf16_host_bits(out))
+    assert np.array_equal(got, O.dequantize(q, s))
+
+
+def test_quantize_empty_and_errors():
+    q, s = moe.mxfp4_quantize(torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda"))
+    assert q.shape == (0, 32) and s.shape == (0, 2)
+    with pytest.raises(moe.MoEError):
+        moe.mxfp4_quantize(torch.zeros(4, 48, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(moe.MoEError):
+        moe.mxfp4_quantize(torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda"), rule=3)
+
+
+# ------------------------------------------------------------------ routing
+
+def gpu_route(x, wr, b, k):
+    r = moe.moe_route(G.bf16_dev(x), G.f32_dev(wr), None if b is None else G.f32_dev(b), k,
+                      with_logits=True)
+    torch.cuda.synchronize()
+    return {f: getattr(r, f).cpu().numpy() for f in
+            ("ids", "weights", "counts", "offsets", "sorted_pairs", "pair_pos", "logits")}
+
+
+def check_route(x, wr, b, k, what):
+    g = gpu_route(x, wr, b, k)
+    ref = O.route(x, wr, b, k)
+    T, E = ref["logits"].shape
+    # logits: fp32 sum of D products against the fp64 one
+    mag = G.bf16_bits_to_f64(x).__abs__() @ np.abs(wr.astype(np.float64)).T
+    assert np.all(np.abs(g["logits"] - ref["logits"]) <= 3e-5 * mag + 1e-6), what
+    near = ref["gap"] < NEAR_TIE
+    ok = ~near
+    assert np.array_equal(g["ids"][ok], ref["ids"][ok]), what
+    # softmax over the selected logits: |dw_j| <= w_j (|dL_j| + sum_i w_i |dL_i|)
+    # <= 2 w_j max_i |dL_i|, plus a few fp32 roundings of exp and the division
+    dl = np.abs(np.take_along_axis(g["logits"] - ref["logits"], ref["ids"], 1)).max(1)
+    wbound = 2.0 * ref["w"] * dl[:, None] + 8 * 2.0 ** -24 * ref["w"] + 2.0 ** -26
+    assert np.all(np.abs(g["weights"][ok] - ref["w"][ok]) <= wbound[ok]), what
+    # histogram / offsets / permutation against the GPU's own ids
+    ids = g["ids"].ravel()
+    cnt = np.bincount(ids, minlength=E)
+    assert np.array_equal(g["counts"], cnt), what
+    assert np.array_equal(g["offsets"], np.concatenate([[0], np.cumsum(cnt)])), what
+    assert np.array_equal(g["sorted_pairs"], np.argsort(ids, kind="stable")), what
+    assert np.array_equal(g["pair_pos"][g["sorted_pairs"]], np.arange(T * k)), what
+    if not near.any():
+        for a, b_ in (("counts", "counts"), ("offsets", "offsets"),
+                      ("sorted_pairs", "sorted"), ("pair_pos", "pos")):
+            assert np.array_equal(g[a], ref[b_]), (what, a)
+    log("%s: T=%d E=%d k=%d near-tie tokens excluded: %d" % (what, T, E, k, int(near.sum())))
+    return g, ref
+
+
+ROUTE_CASES = ([("tiny", s) for s in range(10)] +
+               [("gptoss20b_decode", s) for s in range(3)] +
+               [("gptoss120b_decode", s) for s in range(3)] +
+               [("gptoss20b_prefill", 0), ("gptoss120b_prefill_skewed", 0)])
+
+
+@pytest.mark.parametrize("name,seed", ROUTE_CASES)
+def test_route_workloads(name, seed):
+    cfg = MI.CONFIGS[name]
+    wr, b = MI.gen_router(cfg, seed)
+    check_route(MI.gen_x(cfg, seed), wr, b, cfg.k, "%s/seed%d" % (name, seed))
+
+
+@pytest.mark.parametrize("T,D,E,k", [(1, 32, 1, 1), (1, 64, 8, 8), (200, 96, 16, 3),
+                                     (130, 64, 256, 8), (65, 32, 5, 5), (4096, 128, 64, 4),
+                                     (333, 2880, 128, 4)])
+def test_route_shapes(T, D, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    x = MI.f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    wr = (rng.standard_normal((E, D)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    check_route(x, wr, b, k, "shape T=%d D=%d E=%d k=%d" % (T, D, E, k))
+
+
+def test_route_exact_ties_go_to_lower_id():
+    T, D, E, k = 70, 64, 12, 4
+    x = np.zeros((T, D), np.uint16)
+    wr = np.ones((E, D), np.float32)
+    b = np.array([0.5, 2, 2, 1, 2, 0, 1, 1, 3, 0.5, 2, 3], np.float32)
+    g = gpu_route(x, wr, b, k)
+    assert np.array_equal(g["ids"], np.tile([8, 11, 1, 2], (T, 1)))
+    ref = O.route(x, wr, b, k)
+    for a, b_ in (("ids", "ids"), ("counts", "counts"), ("offsets", "offsets"),
+                  ("sorted_pairs", "sorted"), ("pair_pos", "pos")):
+        assert np.array_equal(g[a], ref[b_]), a
+
+
+# ------------------------------------------------------------------ full layer
+
+class Inputs:
+    def __init__(self, cfg, seed):
+        self.cfg = cfg
+        self.wr, self.b = MI.gen_router(cfg, seed)
+        self.x = MI.gen_x(cfg, seed)
+        self.w13, self.w2 = MI.gen_experts(cfg, seed, threads=G.THREADS)
+
+
+def run_gpu_layer(inp):
+    cfg = inp.cfg
+    xd = G.bf16_dev(inp.x)
+    weights = moe.ExpertWeights.quantize(G.bf16_dev(inp.w13), G.bf16_dev(inp.w2))
+    r = moe.moe_route(xd, G.f32_dev(inp.wr), G.f32_dev(inp.b), cfg.k)
+    out = moe.moe_expert_mlp(xd, weights, r)
+    torch.cuda.synchronize()
+    return weights, r, out
+
+
+def sample_tokens(ids, T, rng, n_random=12):
+    toks = set(range(min(4, T))) | set(range(max(0, T - 4), T))
+    flat = ids.ravel()
+    cnt = np.bincount(flat)
+    hot = int(cnt.argmax())
+    toks |= set((np.nonzero((ids == hot).any(1))[0][:4]).tolist())
+    for e in np.argsort(np.where(cnt > 0, cnt, 1 << 30))[:8]:
+        if cnt[e] > 0:
+            toks.add(int(np.nonzero((ids == e).any(1))[0][0]))
+    toks |= set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    return np.array(sorted(toks))
+
+
+def check_layer(inp, tokens="all", what=""):
+    cfg = inp.cfg
+    weights, r, out = run_gpu_layer(inp)
+    ref_r = O.route(inp.x, inp.wr, inp.b, cfg.k)
+    ok_tok = np.nonzero(ref_r["gap"] >= NEAR_TIE)[0]
+    gids = r.ids.cpu().numpy()
+    assert np.array_equal(gids[ok_tok], ref_r["ids"][ok_tok]), what
+    if tokens == "sample":
+        toks = sample_tokens(ref_r["ids"], cfg.T, np.random.default_rng(5))
+        toks = np.intersect1d(toks, ok_tok)
+    else:
+        toks = ok_tok
+    gq13, gs13 = weights.w13_q.cpu().numpy(), weights.w13_s.cpu().numpy()
+    gq2, gs2 = weights.w2_q.cpu().numpy(), weights.w2_s.cpu().numpy()
+    mismatched = []
+
+    def expert_weights(e):
+        q13, s13 = O.quantize(inp.w13[e])
+        q2, s2 = O.quantize(inp.w2[e])
+        if not (np.array_equal(q13, gq13[e]) and np.array_equal(s13, gs13[e]) and
+                np.array_equal(q2, gq2[e]) and np.array_equal(s2, gs2[e])):
+            mismatched.append(e)
+        return q13, s13, q2, s2
+
+    ref = O.moe_threaded(inp.x, expert_weights, ref_r["ids"], ref_r["w"], cfg.F, tokens=toks,
+                         threads=G.THREADS)
+    assert not mismatched, "%s: quantized experts differ: %s" % (what, mismatched[:8])
+    got = G.bf16_host_bits(out)[toks]
+    worst = G.assert_within_tolerance(got, ref, what)
+    log("%s: %d tokens compared, max err/tol = %.3f" % (what, len(toks), worst))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_layer_tiny(seed):
+    check_layer(Inputs(MI.CONFIGS["tiny"], seed), what="tiny/seed%d" % seed)
+
+
+@pytest.mark.parametrize("name,tokens", [("gptoss20b_decode", "all"),
+                                         ("gptoss120b_decode", "all"),
+                                         ("gptoss20b_prefill", "sample"),
+                                         ("gptoss120b_prefill_skewed", "sample")])
+def test_layer_workloads(name, tokens):
+    check_layer(Inputs(MI.CONFIGS[name], 0), tokens=tokens, what=name)
+
+
+EDGE = [
+    MI.MoEConfig("ragged", T=37, D=96, F=160, E=6, k=2),
+    MI.MoEConfig("one_expert_many_tokens", T=70, D=64, F=64, E=1, k=1),
+    MI.MoEConfig("k_equals_E", T=20, D=128, F=96, E=4, k=4),
+    MI.MoEConfig("single_token_full_width", T=1, D=2880, F=2880, E=32, k=4),
+    MI.MoEConfig("wide_router", T=300, D=64, F=32, E=256, k=8),
+    MI.MoEConfig("long_contraction_D", T=9, D=4096, F=64, E=2, k=1),
+    MI.MoEConfig("long_contraction_F", T=9, D=64, F=4096, E=2, k=2),
+    MI.MoEConfig("outliers_small", T=40, D=256, F=128, E=8, k=2, outliers=True),
+    MI.MoEConfig("zipf_small", T=500, D=64, F=64, E=32, k=4, bias="zipf"),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
+def test_layer_edge_shapes(cfg):
+    check_layer(Inputs(cfg, 3), what=cfg.name)
+
+
+def test_layer_is_deterministic():
+    inp = Inputs(MI.CONFIGS["gptoss20b_decode"], 1)
+    _, _, a = run_gpu_layer(inp)
+    _, _, b = run_gpu_layer(inp)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_moe_layer_object_matches_calls():
+    inp = Inputs(MI.CONFIGS["tiny"], 2)
+    cfg = inp.cfg
+    weights, r, out = run_gpu_layer(inp)
+    layer = moe.MoELayer(G.f32_dev(inp.wr), G.f32_dev(inp.b), weights, cfg.k, cfg.T)
+    out2 = layer(G.bf16_dev(inp.x))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))

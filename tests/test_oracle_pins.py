@@ -376,3 +376,17 @@ def test_tiny_workload_has_no_near_ties():
     r = O.route(MI.gen_x(cfg, 0), wr, b, cfg.k)
     assert r["gap"].min() > 1e-4
     assert r["counts"].sum() == cfg.P
+
+
+def test_threaded_harness_equals_plain_oracle():
+    T, D, F, E, k = 9, 64, 96, 5, 2
+    x, wr, b = _tiny_router(T=T, D=D, E=E, seed=19)
+    q13, s13, q2, s2 = _tiny_experts(E, D, F, seed=20)
+    r = O.route(x, wr, b, k)
+    plain = O.moe(x, q13, s13, q2, s2, r["ids"], r["w"], F)
+    thr = O.moe_threaded(x, lambda e: (q13[e], s13[e], q2[e], s2[e]), r["ids"], r["w"], F,
+                         threads=3)
+    assert np.array_equal(plain, thr)
+    sub = O.moe_threaded(x, lambda e: (q13[e], s13[e], q2[e], s2[e]), r["ids"], r["w"], F,
+                         tokens=[4, 0], threads=2)
+    assert np.array_equal(sub, plain[[4, 0]])
