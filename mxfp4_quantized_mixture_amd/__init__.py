@@ -192,6 +192,17 @@ class ExpertWeights:
         return cls(a, b, c, d)
 
 
+def _event_array(events) -> ctypes.Array:
+    """4 torch.cuda.Event objects -> hipEvent_t[4].  torch creates the native
+    event lazily, on its first record(), so record each once if needed."""
+    if len(events) != 4:
+        raise ValueError("events must hold 4 torch.cuda.Event objects")
+    for e in events:
+        if not e.cuda_event:
+            e.record()
+    return (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+
+
 def mlp_workspace(T: int, D: int, F: int, E: int, k: int, device) -> torch.Tensor:
     n = lib().moe_expert_mlp_workspace_size(T, D, F, E, k)
     if n == 0:
@@ -209,11 +220,7 @@ def moe_expert_mlp(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
         raise ValueError("expert weights do not match d_model")
     out = out if out is not None else torch.empty(T, D, dtype=torch.bfloat16, device=x.device)
     ws = ws if ws is not None else mlp_workspace(T, D, F, E, k, x.device)
-    ev = None
-    if events is not None:
-        if len(events) != 4:
-            raise ValueError("events must hold 4 torch.cuda.Event objects")
-        ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    ev = None if events is None else _event_array(events)
     _check("moe_expert_mlp", lib().moe_expert_mlp(
         _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
         _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
@@ -244,3 +251,48 @@ class MoELayer:
             raise ValueError("MoELayer was sized for %d tokens" % self.max_tokens)
         r = moe_route(x, self.wr, self.br, self.k, out=self.routing, ws=self.route_ws)
         return moe_expert_mlp(x, self.weights, r, out=out, ws=self.mlp_ws, events=events)
+
+
+class PreparedLayer:
+    """Route + experts with every C-ABI argument marshalled once.
+
+    For tight loops (decode steps): calling it only re-issues the two C calls
+    on the stream captured at construction, so the host adds no per-call
+    tensor checks.  Buffers must stay alive and unchanged in shape.
+    """
+
+    def __init__(self, x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None,
+                 weights: ExpertWeights, k: int, out: torch.Tensor, routing: Routing,
+                 route_ws: torch.Tensor, mlp_ws: torch.Tensor, stream=None):
+        T, D = x.shape
+        E, F = weights.E, weights.F
+        self.L = lib()
+        st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
+        self._keep = (x, wr, br, weights, out, routing, route_ws, mlp_ws)
+        self.route_args = (
+            _dev(x, "x", torch.bfloat16), _dev(wr, "wr", torch.float32),
+            None if br is None else _dev(br, "br", torch.float32), T, D, E, k,
+            _dev(routing.ids, "ids"), _dev(routing.weights, "weights"),
+            _dev(routing.counts, "counts"), _dev(routing.offsets, "offsets"),
+            _dev(routing.sorted_pairs, "sorted_pairs"), _dev(routing.pair_pos, "pair_pos"),
+            None, _dev(route_ws, "ws"), route_ws.numel(), st)
+        self.mlp_head = (
+            _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
+            _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
+            _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w"),
+            _dev(routing.offsets, "offsets"), _dev(routing.sorted_pairs, "sorted_pairs"),
+            _dev(routing.pair_pos, "pair_pos"), T, D, F, E, k, _dev(out, "out", torch.bfloat16),
+            _dev(mlp_ws, "ws"), mlp_ws.numel())
+        self.stream = st
+
+    @staticmethod
+    def event_array(events) -> ctypes.Array:
+        return _event_array(events)
+
+    def __call__(self, event_array=None) -> None:
+        s = self.L.moe_route(*self.route_args)
+        if s:
+            raise MoEError("moe_route", s)
+        s = self.L.moe_expert_mlp(*self.mlp_head, event_array, self.stream)
+        if s:
+            raise MoEError("moe_expert_mlp", s)

@@ -1,7 +1,7 @@
 // api.hip -- the exported C ABI of libmoe_mxfp4 (declared in
 // include/moe_mxfp4.h): argument validation, workspace carving, launches.
 // Every check happens before anything is enqueued.
-#include "../../include/moe_mxfp4.h"
+#include "moe_mxfp4.h"
 #include "launch.h"
 
 namespace {
@@ -91,8 +91,8 @@ moe_status_t moe_expert_mlp(const uint16_t* x, const uint8_t* w13_q, const uint8
         return MOE_ERR_NULL;
     const moe::MlpPlan plan = moe::plan_mlp(T, D, F, E, k);
     if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
-    if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(out) ||
-        !aligned16(ws))
+    if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
+        !aligned16(w2_s) || !aligned16(out) || !aligned16(ws))
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_mlp(plan, x, w13_q, w13_s, w2_q, w2_s, topk_w, offsets,
                                       sorted_pairs, pair_pos, out, ws, stage_events, stream));

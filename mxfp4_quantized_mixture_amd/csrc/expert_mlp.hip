@@ -20,6 +20,9 @@
 // products, 8 per product.  The A (weights) and B (activations) operands use
 // the same permutation, so the contraction is unchanged, and every lane loads
 // one whole 16-byte block of codes plus its one scale byte.
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -199,6 +202,388 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced weight-streaming kernels.
+//
+// A "unit" is one expert with up to 16 of its tokens (experts with more tokens
+// contribute several units).  Work = units x 16-row weight tiles, split evenly
+// over the grid; every block builds the unit table from `offsets` itself, so
+// no host synchronisation is needed.  For each unit in its range a block
+// stages the unit's activation rows in LDS once; each wavefront then owns
+// whole tiles over the full contraction dimension (no cross-wave reduction)
+// and keeps two batches of weight loads in flight.
+// ---------------------------------------------------------------------------
+
+constexpr int kStreamWaves = 8;
+constexpr int kNB = 4;                 // super-steps per load batch
+
+struct UnitTable {
+    int* units_before;                 // [E + 1] in LDS
+    int total;                         // number of units
+};
+
+// units_before[e] = sum over e' < e of ceil(n_e' / 16); needs >= 256 threads.
+__device__ void build_unit_table(const int32_t* __restrict__ offsets, int E, int* ub, int* wsum) {
+    const int tid = threadIdx.x;
+    int v = 0;
+    if (tid < E) v = (offsets[tid + 1] - offsets[tid] + 15) >> 4;
+    const int lane = tid & 63, wave = tid >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int n = __shfl_up(incl, off);
+        if (lane >= off) incl += n;
+    }
+    if (wave < 4 && lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (tid < 256) {
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wsum[w];
+        if (tid < E) ub[tid] = base + incl - v;
+        if (tid == E - 1) ub[E] = base + incl;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ int unit_expert(const int* ub, int E, int u) {
+    int lo = 0, hi = E - 1;            // largest e with ub[e] <= u
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ub[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Staged activations.  The weights enter the matrix cores exactly as stored
+// (E2M1 codes + E8M0 block scales, v_mfma_scale_f32_16x16x128_f8f6f4 with an
+// fp4 A operand), so the activations must be fp8: each activation row is
+// split into NT E4M3 terms, term t+1 carrying the rounding residual of term
+// t, each with its own E8M0 scale per 32-element block.  A value with b
+// significant bits is represented exactly by ceil(b / 4) terms when it lies
+// within 13 binades of its block's largest magnitude (bf16 x: 2 terms;
+// fp16 h: 3 terms); smaller elements keep an error below 2^-21 of that
+// magnitude.
+//
+// Operand layouts of the 16x16x128 scaled product (lane l, m = l % 16,
+// g = l / 16): A lane holds row m, K = 32 g .. 32 g + 31 (one MXFP4 block,
+// low nibble first) and that block's scale; B lane holds column m, bytes
+// 0..15 = K 16 g .. 16 g + 15 and bytes 16..31 = K 64 + 16 g .. + 15, and
+// the scale of K-block g of column m.  C is as for the 16x16x32 products.
+//
+// LDS, per unit: data [nss][NT][64 lanes][32 B], then scales [nss][NT][64].
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+__device__ __forceinline__ f32x4_t mfma_fp4w_fp8x(u32x4_t w, int wscale, const u32x4_t (&b)[2],
+                                                 int bscale, f32x4_t c) {
+    i32x8_t a8 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+    i32x8_t b8 = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                  (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+    // cbsz = 4: A is fp4 (e2m1); blgp = 0: B is fp8 (e4m3)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 0, 0, wscale, 0, bscale);
+}
+
+__device__ __forceinline__ float act_to_f32(uint16_t v, bool is_bf16) {
+    return is_bf16 ? __builtin_bit_cast(float, (uint32_t)v << 16)
+                   : (float)__builtin_bit_cast(_Float16, v);
+}
+
+// Stage the unit's rows (pairs row0 .. row0 + nvalid - 1 in sorted order;
+// gathered bf16 x rows for gate/up, contiguous fp16 h rows for down) as NT
+// fp8 terms.  One thread per (row, 32-element block); rows past nvalid and
+// blocks past K are zero with scale 2^0.
+template <int NT, bool kGather>
+__device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __restrict__ sorted,
+                            int row0, int nvalid, int k, int K, uint8_t* lds, int* s_row) {
+    if (threadIdx.x < 16)
+        s_row[threadIdx.x] = threadIdx.x < nvalid
+            ? (kGather ? sorted[row0 + threadIdx.x] / k : row0 + threadIdx.x) : -1;
+    __syncthreads();
+    const int nblk = K / 32, nss = (nblk + 3) / 4;
+    uint8_t* scales = lds + (size_t)nss * NT * 64 * 32;
+    for (int task = threadIdx.x; task < 16 * nss * 4; task += blockDim.x) {
+        const int m = task & 15, blk = task >> 4;         // blk < 4 * nss
+        const int ss = blk >> 2, gq = blk & 3;             // block gq of super-step ss
+        const bool live = blk < nblk && s_row[m] >= 0;
+        if (!live) {                                   // padding row or block: zeros, scale 2^0
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    *reinterpret_cast<u32x4_t*>(base + (16 * (2 * (gq & 1) + half) + m) * 32 +
+                                                16 * (gq >> 1)) = z;
+                scales[(ss * NT + t) * 64 + gq * 16 + m] = 127;
+            }
+            continue;
+        }
+        float v[32];
+        {
+            const uint16_t* p = src + (int64_t)s_row[m] * K + blk * 32;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(p + c * 8);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[c * 8 + 2 * h] = act_to_f32((uint16_t)(raw[h] & 0xFFFFu), kGather);
+                    v[c * 8 + 2 * h + 1] = act_to_f32((uint16_t)(raw[h] >> 16), kGather);
+                }
+            }
+        }
+        // Hardware K of element n of block gq is 32 gq + n: lanes 16 * (2 (gq & 1) + n / 16)
+        // + m, byte 16 (gq >> 1) + n % 16.
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float amax = 0.f;
+#pragma unroll
+            for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(v[n]));
+            // s = floor(log2 amax) - 7 puts the block maximum in [128, 256) (E4M3 max 448)
+            int se = amax > 0.f ? (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 7 : 0;
+            se = se < -127 ? -127 : se;
+            const float inv = __builtin_bit_cast(float, (uint32_t)(127 - se) << 23);   // 2^-s, s >= -120
+            const float sc = se >= -126 ? __builtin_bit_cast(float, (uint32_t)(127 + se) << 23)
+                                        : __builtin_bit_cast(float, 0x00400000u);    // 2^s
+            uint32_t q[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w] * inv, v[4 * w + 1] * inv, 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2] * inv, v[4 * w + 3] * inv, pk, true);
+                q[w] = (uint32_t)pk;
+            }
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                v[4 * w] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 0) * sc;
+                v[4 * w + 1] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 1) * sc;
+                v[4 * w + 2] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 2) * sc;
+                v[4 * w + 3] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 3) * sc;
+            }
+            uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int lane = 16 * (2 * (gq & 1) + half) + m;
+                u32x4_t w4 = {q[4 * half], q[4 * half + 1], q[4 * half + 2], q[4 * half + 3]};
+                *reinterpret_cast<u32x4_t*>(base + lane * 32 + 16 * (gq >> 1)) = w4;
+            }
+            scales[(ss * NT + t) * 64 + gq * 16 + m] = (uint8_t)(se + 127);
+        }
+    }
+}
+
+template <int NS>
+struct WBatch {
+    u32x4_t q[NS][kNB];
+};
+
+// Load kNB super-steps (from ss0) of NS weight rows; out-of-range blocks are
+// clamped to the row's last block (finite data, multiplied by zero activations).
+template <int NS>
+__device__ __forceinline__ void load_batch(WBatch<NS>& B, const uint8_t* const (&q)[NS], int ss0,
+                                           int g, int nblk) {
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+        int blk = (ss0 + i) * 4 + g;
+        blk = blk < nblk ? blk : nblk - 1;
+#pragma unroll
+        for (int r = 0; r < NS; ++r) B.q[r][i] = *reinterpret_cast<const u32x4_t*>(q[r] + blk * 16);
+    }
+}
+
+// The E8M0 scales of a 16-row weight tile are one contiguous 16 * nblk-byte
+// run of the [rows, K/32] scale array (16-byte aligned).  A wavefront fetches
+// the next tile's runs into registers while it streams the current tile, and
+// commits them to its own LDS buffer at the tile switch.
+constexpr int kScaleChunks = 2;        // 16-byte chunks per lane: K <= 4096
+
+template <int NS>
+struct ScaleRegs {
+    u32x4_t v[NS][kScaleChunks];
+};
+
+template <int NS>
+__device__ __forceinline__ void fetch_scales(ScaleRegs<NS>& S, const uint8_t* const (&run)[NS],
+                                             int lane, int nblk) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int c = 0; c < kScaleChunks; ++c) {
+            const int idx = lane + 64 * c;    // 16-byte chunk of the 16 * nblk-byte run
+            S.v[r][c] = u32x4_t{0u, 0u, 0u, 0u};
+            if (idx < nblk) S.v[r][c] = *reinterpret_cast<const u32x4_t*>(run[r] + idx * 16);
+        }
+}
+
+template <int NS>
+__device__ __forceinline__ void commit_scales(const ScaleRegs<NS>& S, uint8_t* buf, int lane,
+                                              int nblk) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int c = 0; c < kScaleChunks; ++c) {
+            const int idx = lane + 64 * c;
+            if (idx < nblk) *reinterpret_cast<u32x4_t*>(buf + r * 16 * nblk + idx * 16) = S.v[r][c];
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NS, int NT>
+__device__ __forceinline__ void compute_batch(const WBatch<NS>& B, int ss0, int nss,
+                                              const uint8_t* lds, const uint8_t* lds_scales,
+                                              const uint8_t* wsc, int lane, int g, int nblk,
+                                              f32x4_t (&acc)[NS]) {
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+        const int ss = ss0 + i;
+        if (ss < nss) {
+            int blk = ss * 4 + g;
+            blk = blk < nblk ? blk : nblk - 1;
+            int wscale[NS];
+#pragma unroll
+            for (int r = 0; r < NS; ++r) wscale[r] = wsc[r * 16 * nblk + blk];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint8_t* frag = lds + ((size_t)(ss * NT + t) * 64 + lane) * 32;
+                u32x4_t bx[2];
+                bx[0] = *reinterpret_cast<const u32x4_t*>(frag);
+                bx[1] = *reinterpret_cast<const u32x4_t*>(frag + 16);
+                const int bs = lds_scales[(ss * NT + t) * 64 + lane];
+#pragma unroll
+                for (int r = 0; r < NS; ++r)
+                    acc[r] = mfma_fp4w_fp8x(B.q[r][i], wscale[r], bx, bs, acc[r]);
+            }
+        }
+    }
+}
+
+// kGateUp: A = [gate rows; up rows] of W13 (NS = 2), B = x rows (2 fp8 terms),
+//          epilogue h = silu(g) * u -> fp16.
+// else:    A = W2 rows (NS = 1), B = h rows (3 fp8 terms), epilogue y -> fp32.
+template <bool kGateUp>
+__global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
+    const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ ws, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted, int D, int F, int E, int k,
+    void* __restrict__ out) {
+    constexpr int NS = kGateUp ? 2 : 1;
+    constexpr int NT = kGateUp ? 2 : 3;
+    extern __shared__ __align__(16) uint8_t lds_stage[];
+    __shared__ int ub[257];
+    __shared__ int wsum[4];
+    __shared__ int s_row[16];
+    build_unit_table(offsets, E, ub, wsum);
+    const int K = kGateUp ? D : F;           // contraction length
+    const int NOUT = kGateUp ? F : D;        // output features (per stream)
+    const int ntiles = NOUT / 16;
+    const int64_t total = (int64_t)ub[E] * ntiles;
+    const int64_t t_beg = total * blockIdx.x / gridDim.x;
+    const int64_t t_end = total * (blockIdx.x + 1) / gridDim.x;
+    if (t_beg >= t_end) return;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int nblk = K / 32, nss = (nblk + 3) / 4, nbt = (nss + kNB - 1) / kNB;
+    const size_t rowbytes = (size_t)K / 2;
+    const uint8_t* lds_scales = lds_stage + (size_t)nss * NT * 64 * 32;
+    uint8_t* wave_sc = lds_stage + (size_t)nss * NT * 64 * 33 + (size_t)wave * NS * 16 * nblk;
+    const uint8_t* wsc = wave_sc + m * nblk;        // this lane's row of the committed run
+
+    for (int64_t seg = t_beg; seg < t_end;) {
+        const int u = (int)(seg / ntiles);
+        const int64_t seg_end = min(t_end, (int64_t)(u + 1) * ntiles);
+        const int e = unit_expert(ub, E, u);
+        const int tg = u - ub[e];
+        const int row0 = offsets[e] + tg * 16;
+        const int nvalid = min(16, offsets[e + 1] - row0);
+        const int a = (int)(seg - (int64_t)u * ntiles), b = (int)(seg_end - (int64_t)u * ntiles);
+        const int my_tiles = a + wave < b ? (b - a - wave + kStreamWaves - 1) / kStreamWaves : 0;
+        const int steps = my_tiles * nbt;
+        const uint8_t* qe = wq + (size_t)e * (kGateUp ? 2 * F : D) * rowbytes;
+        const uint8_t* se = ws + (size_t)e * (kGateUp ? 2 * F : D) * nblk;
+
+        auto rows_of = [&](int s, const uint8_t* (&q)[NS]) {
+            const int tile = a + wave + (s / nbt) * kStreamWaves;
+#pragma unroll
+            for (int r = 0; r < NS; ++r) {
+                const int row = r * F + tile * 16 + m;     // up rows follow the F gate rows
+                q[r] = qe + (size_t)row * rowbytes;
+            }
+        };
+        auto runs_of = [&](int tile, const uint8_t* (&run)[NS]) {
+#pragma unroll
+            for (int r = 0; r < NS; ++r) run[r] = se + (size_t)(r * F + tile * 16) * nblk;
+        };
+        auto epilogue = [&](int s, f32x4_t (&acc)[NS]) {
+            const int tile = a + wave + (s / nbt) * kStreamWaves;
+            if (m < nvalid) {
+                if constexpr (kGateUp) {
+                    typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
+                    f16x4_t hv;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) hv[q] = (_Float16)(silu_f32(acc[0][q]) * acc[1][q]);
+                    *reinterpret_cast<f16x4_t*>(static_cast<_Float16*>(out) +
+                                                (size_t)(row0 + m) * F + tile * 16 + 4 * g) = hv;
+                } else {
+                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) +
+                                                (size_t)(row0 + m) * D + tile * 16 + 4 * g) = acc[0];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        };
+
+        f32x4_t acc[NS];
+#pragma unroll
+        for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // Ring of three weight batches.  Prefetches are unconditional (steps past
+        // the end reload the last step's lines, which are cache hits) so the
+        // compiler never has to drain the load queue at a branch; only the
+        // compute is predicated.
+        const int last = steps > 0 ? steps - 1 : 0;
+        auto fetch = [&](WBatch<NS>& W, int s) {
+            const int sc_ = s < last ? s : last;
+            const uint8_t* q[NS];
+            rows_of(sc_, q);
+            load_batch<NS>(W, q, (sc_ % nbt) * kNB, g, nblk);
+        };
+        ScaleRegs<NS> SR;
+        auto consume = [&](const WBatch<NS>& W, int s) {
+            if (s % nbt == 0) {               // tile switch: commit its scales, fetch the next's
+                commit_scales<NS>(SR, wave_sc, lane, nblk);
+                const int nxt = s + nbt < steps ? s + nbt : s;
+                const uint8_t* run[NS];
+                runs_of(a + wave + (nxt / nbt) * kStreamWaves, run);
+                fetch_scales<NS>(SR, run, lane, nblk);
+            }
+            compute_batch<NS, NT>(W, (s % nbt) * kNB, nss, lds_stage, lds_scales, wsc, lane, g,
+                                  nblk, acc);
+            if (s % nbt == nbt - 1) epilogue(s, acc);
+        };
+        WBatch<NS> B0, B1, B2;
+        if (steps > 0) {          // first weights in flight while the activations are staged
+            const uint8_t* run[NS];
+            runs_of(a + wave, run);
+            fetch_scales<NS>(SR, run, lane, nblk);
+            fetch(B0, 0);
+            fetch(B1, 1);
+            fetch(B2, 2);
+        }
+        __syncthreads();                       // previous unit's rows no longer read
+        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row);
+        __syncthreads();
+        for (int s = 0; s < steps; s += 3) {
+            consume(B0, s);
+            fetch(B0, s + 3);
+            if (s + 1 < steps) consume(B1, s + 1);
+            fetch(B1, s + 4);
+            if (s + 2 < steps) consume(B2, s + 2);
+            fetch(B2, s + 5);
+        }
+        seg = seg_end;
+    }
+}
+
 // out[t, d] = bf16( sum_j w[t, j] * y[pos[t*k + j], d] ), slots in order.
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, const float* __restrict__ topk_w,
@@ -235,6 +620,23 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     return p;
 }
 
+constexpr size_t kMaxStreamLds = 158 * 1024;   // of 160 KiB, leaving room for static LDS
+
+// Staged fp8 terms of 16 rows of K elements: ceil(K/128) super-steps x NT
+// terms x 64 lanes x (32 data bytes + 1 scale byte).
+static size_t stream_lds_bytes(int K, int NT, int NS) {
+    return (size_t)((K / 32 + 3) / 4) * NT * 64 * 33 + (size_t)kStreamWaves * NS * 16 * (K / 32);
+}
+
+// One round of blocks over the 256 CUs of MI355X (two blocks per CU when the
+// staged rows leave room for two), never more than one block per 8 tiles.
+static int stream_grid(int64_t tiles_upper, size_t lds_bytes) {
+    const int per_cu = lds_bytes * 2 <= kMaxStreamLds ? 2 : 1;
+    int64_t g = (tiles_upper + kStreamWaves - 1) / kStreamWaves;
+    if (g > 256 * per_cu) g = 256 * per_cu;
+    return (int)(g < 1 ? 1 : g);
+}
+
 static int blocks_per_expert(int E, int ntiles) {
     int bpe = (2048 + E - 1) / E;
     if (bpe > ntiles) bpe = ntiles;
@@ -253,16 +655,44 @@ hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
         const hipError_t er = hipEventRecord(events[0], stream);
         if (er != hipSuccess) return er;
     }
-    const int bpe1 = blocks_per_expert(p.E, p.F / 16);
-    hipLaunchKernelGGL(gateup_stream_kernel, dim3(p.E * bpe1), dim3(256), 0, stream, x, w13q,
-                       w13s, offsets, sorted, p.D, p.F, p.k, bpe1, h);
-    if (events) {
-        const hipError_t er = hipEventRecord(events[1], stream);
-        if (er != hipSuccess) return er;
+    const int64_t P = (int64_t)p.T * p.k;
+    const int64_t units_max = std::min<int64_t>(P, (P + 15) / 16 + p.E);
+    const size_t lds_gu = stream_lds_bytes(p.D, 2, 2), lds_dn = stream_lds_bytes(p.F, 3, 1);
+    if (lds_gu <= kMaxStreamLds && lds_dn <= kMaxStreamLds && p.D <= 4096 && p.F <= 4096) {
+        const int g1 = stream_grid(units_max * (p.F / 16), lds_gu);
+        if (lds_gu > 65536) {
+            hipError_t er = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<true>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu);
+            if (er != hipSuccess) return er;
+        }
+        hipLaunchKernelGGL(expert_stream_kernel<true>, dim3(g1), dim3(kStreamWaves * 64), lds_gu,
+                           stream, x, w13q, w13s, offsets, sorted, p.D, p.F, p.E, p.k,
+                           static_cast<void*>(h));
+        if (events) {
+            const hipError_t er = hipEventRecord(events[1], stream);
+            if (er != hipSuccess) return er;
+        }
+        const int g2 = stream_grid(units_max * (p.D / 16), lds_dn);
+        if (lds_dn > 65536) {
+            hipError_t er = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<false>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn);
+            if (er != hipSuccess) return er;
+        }
+        hipLaunchKernelGGL(expert_stream_kernel<false>, dim3(g2), dim3(kStreamWaves * 64), lds_dn,
+                           stream, reinterpret_cast<const uint16_t*>(h), w2q, w2s, offsets, sorted,
+                           p.D, p.F, p.E, p.k, static_cast<void*>(y));
+    } else {
+        const int bpe1 = blocks_per_expert(p.E, p.F / 16);
+        hipLaunchKernelGGL(gateup_stream_kernel, dim3(p.E * bpe1), dim3(256), 0, stream, x, w13q,
+                           w13s, offsets, sorted, p.D, p.F, p.k, bpe1, h);
+        if (events) {
+            const hipError_t er = hipEventRecord(events[1], stream);
+            if (er != hipSuccess) return er;
+        }
+        const int bpe2 = blocks_per_expert(p.E, p.D / 16);
+        hipLaunchKernelGGL(down_stream_kernel, dim3(p.E * bpe2), dim3(256), 0, stream, h, w2q,
+                           w2s, offsets, p.D, p.F, bpe2, y);
     }
-    const int bpe2 = blocks_per_expert(p.E, p.D / 16);
-    hipLaunchKernelGGL(down_stream_kernel, dim3(p.E * bpe2), dim3(256), 0, stream, h, w2q, w2s,
-                       offsets, p.D, p.F, bpe2, y);
     if (events) {
         const hipError_t er = hipEventRecord(events[2], stream);
         if (er != hipSuccess) return er;

@@ -14,9 +14,10 @@ hipError_t launch_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, i
 
 struct RoutePlan {
     int T, D, E, k;
-    int splits;        // D-slices of the router product (partial sums)
+    int token_tiles;   // 16-token tiles per router block
+    int splits;        // slices of the router contraction (partial logits summed in order)
     int chunks;        // token chunks of the top-k / histogram pass
-    size_t off_partial, off_chunk_counts, off_chunk_base, ws_bytes;
+    size_t off_logits, off_chunk_counts, off_chunk_base, ws_bytes;
 };
 RoutePlan plan_route(int T, int D, int E, int k);
 hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, const float* br,

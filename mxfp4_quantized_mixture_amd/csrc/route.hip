@@ -8,10 +8,10 @@
 // so that the expert GEMMs read contiguous row ranges.
 //
 // Kernels:
-//   router_partial_kernel  logits as fp32 partial sums over D-slices
-//                          (32x32 output tiles, LDS-staged operands)
-//   route_topk_kernel      one wavefront per token: sum of the slices + bias,
-//                          k rounds of wave-wide argmax, softmax, LDS histogram
+//   router_logits_kernel   matrix-core logits (fp32 weights as 3 exact bf16
+//                          terms), split-K over 16 wavefronts
+//   route_topk_kernel      one wavefront per token: k rounds of wave-wide
+//                          argmax, softmax over the k, LDS histogram
 //                          per 64-token chunk; with a single chunk it also runs
 //                          the scan and the scatter (one launch for decode)
 //   route_scan_kernel      per-expert running sums over chunks + block scan
@@ -24,56 +24,115 @@
 
 namespace moe {
 
-constexpr int kRouteTile = 32;     // tokens x experts per router tile
 constexpr int kChunkTokens = 64;   // tokens per top-k / histogram chunk
 constexpr int kMaxK = 8;
 constexpr int kMaxE = 256;
 
-__global__ __launch_bounds__(256) void router_partial_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr,
-    float* __restrict__ partial, int T, int D, int E, int splits) {
-    __shared__ float xs[kRouteTile][kRouteTile + 1];
-    __shared__ float ws[kRouteTile][kRouteTile + 1];
-    const int t0 = blockIdx.x * kRouteTile, e0 = blockIdx.y * kRouteTile, sp = blockIdx.z;
-    const int nch = D / 32;
-    const int c_begin = (int)((int64_t)nch * sp / splits);
-    const int c_end = (int)((int64_t)nch * (sp + 1) / splits);
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int lr = tid >> 3, lc = (tid & 7) * 4;
-    float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
-    for (int c = c_begin; c < c_end; ++c) {
-        const int d0 = c * 32;
-        const int t = t0 + lr, e = e0 + lr;
-        uint2 xv = make_uint2(0u, 0u);
-        if (t < T) xv = *reinterpret_cast<const uint2*>(x + (int64_t)t * D + d0 + lc);
-        float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e < E) wv = *reinterpret_cast<const float4*>(wr + (int64_t)e * D + d0 + lc);
-        xs[lr][lc + 0] = bf16_to_f32(xv.x & 0xFFFFu);
-        xs[lr][lc + 1] = bf16_to_f32(xv.x >> 16);
-        xs[lr][lc + 2] = bf16_to_f32(xv.y & 0xFFFFu);
-        xs[lr][lc + 3] = bf16_to_f32(xv.y >> 16);
-        ws[lr][lc + 0] = wv.x;
-        ws[lr][lc + 1] = wv.y;
-        ws[lr][lc + 2] = wv.z;
-        ws[lr][lc + 3] = wv.w;
-        __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < 32; ++dd) {
-            const float x0 = xs[ty][dd], x1 = xs[ty + 16][dd];
-            const float w0 = ws[tx][dd], w1 = ws[tx + 16][dd];
-            a00 = __builtin_fmaf(x0, w0, a00);
-            a01 = __builtin_fmaf(x0, w1, a01);
-            a10 = __builtin_fmaf(x1, w0, a10);
-            a11 = __builtin_fmaf(x1, w1, a11);
+// Router logits on the matrix cores.  Each fp32 router weight is split
+// exactly into three bf16 terms by truncation, w = hi + mid + lo: hi keeps
+// the top 16 bits of w, mid the top 16 bits of the (exact) residual, and lo
+// the remaining at most 8 significant bits.  The activations are bf16, so the
+// three 16x16x32 bf16 products accumulate x . w with fp32 rounding only.
+// Grid: 16-expert tiles x (16 * TT)-token tiles x S slices of the
+// contraction; each block's 4 wavefronts split its slice further and are
+// summed through LDS in a fixed order.  Slice s writes its partial tile to
+// P[s]; slice 0 adds the bias.  The top-k kernel sums the S slices in order.
+constexpr int kRouterWaves = 4;
+
+__device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8_t& hi, bf16x8_t& mid,
+                                            bf16x8_t& lo) {
+    u32x4_t h, md, l;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t u = __builtin_bit_cast(uint32_t, w[2 * p + q]);
+            hb[q] = u & 0xFFFF0000u;
+            const uint32_t r1 = __builtin_bit_cast(uint32_t, w[2 * p + q] - __builtin_bit_cast(float, hb[q]));
+            mb[q] = r1 & 0xFFFF0000u;
+            lb[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, r1) - __builtin_bit_cast(float, mb[q]));
         }
-        __syncthreads();
+        h[p] = (hb[0] >> 16) | hb[1];
+        md[p] = (mb[0] >> 16) | mb[1];
+        l[p] = (lb[0] >> 16) | (lb[1] & 0xFFFF0000u);
     }
-    float* base = partial + (int64_t)sp * T * E;
-    const int ta = t0 + ty, tb = t0 + ty + 16, ea = e0 + tx, eb = e0 + tx + 16;
-    if (ta < T && ea < E) base[(int64_t)ta * E + ea] = a00;
-    if (ta < T && eb < E) base[(int64_t)ta * E + eb] = a01;
-    if (tb < T && ea < E) base[(int64_t)tb * E + ea] = a10;
-    if (tb < T && eb < E) base[(int64_t)tb * E + eb] = a11;
+    hi = as_bf16x8(h);
+    mid = as_bf16x8(md);
+    lo = as_bf16x8(l);
+}
+
+template <int TT>
+__global__ __launch_bounds__(kRouterWaves * 64) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
+    float* __restrict__ P, int T, int D, int E, int S) {
+    __shared__ f32x4_t red[kRouterWaves][TT][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * TT, sl = blockIdx.z;
+    const int nk = D / 32;
+    const int part = sl * kRouterWaves + wave, parts = S * kRouterWaves;
+    const int k_beg = (int)((int64_t)nk * part / parts), k_end = (int)((int64_t)nk * (part + 1) / parts);
+    const int e = e0 + m;
+    const bool eok = e < E;
+    const float* wrow = wr + (int64_t)(eok ? e : 0) * D;
+    f32x4_t acc[TT];
+#pragma unroll
+    for (int u = 0; u < TT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int KB = 4;                       // K-steps whose loads are issued together
+    for (int kk = k_beg; kk < k_end; kk += KB) {
+        float4 wa[KB], wb[KB];
+        u32x4_t xv[KB][TT];
+#pragma unroll
+        for (int h = 0; h < KB; ++h) {
+            const int off = (kk + h) * 32 + 8 * g;
+            const bool kok = kk + h < k_end;
+            wa[h] = wb[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kok && eok) {
+                wa[h] = *reinterpret_cast<const float4*>(wrow + off);
+                wb[h] = *reinterpret_cast<const float4*>(wrow + off + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < TT; ++u) {
+                const int t = t0 + 16 * u + m;
+                xv[h][u] = u32x4_t{0u, 0u, 0u, 0u};
+                if (kok && t < T) xv[h][u] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * D + off);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < KB; ++h) {
+            if (kk + h < k_end) {
+                const float w[8] = {wa[h].x, wa[h].y, wa[h].z, wa[h].w,
+                                    wb[h].x, wb[h].y, wb[h].z, wb[h].w};
+                bf16x8_t hi, mid, lo;
+                split3_bf16(w, hi, mid, lo);
+#pragma unroll
+                for (int u = 0; u < TT; ++u) {
+                    const bf16x8_t xb = as_bf16x8(xv[h][u]);
+                    acc[u] = mfma_bf16(hi, xb, acc[u]);
+                    acc[u] = mfma_bf16(mid, xb, acc[u]);
+                    acc[u] = mfma_bf16(lo, xb, acc[u]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < TT; ++u) red[wave][u][lane] = acc[u];
+    __syncthreads();
+    // lane holds C[expert 4g + r][token m] of each token tile
+    float* Ps = P + (int64_t)sl * T * E;
+    for (int u = wave; u < TT; u += kRouterWaves) {
+        f32x4_t sum = red[0][u][lane];
+        for (int w2 = 1; w2 < kRouterWaves; ++w2) sum += red[w2][u][lane];
+        const int t = t0 + 16 * u + m;
+        if (t < T) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ee = e0 + 4 * g + r;
+                if (ee < E) Ps[(int64_t)t * E + ee] = sum[r] + ((br && sl == 0) ? br[ee] : 0.f);
+            }
+        }
+    }
 }
 
 // (v1, i1) ranks before (v2, i2): larger logit, then lower expert id.
@@ -81,7 +140,7 @@ __device__ __forceinline__ bool ranks_before(float v1, int i1, float v2, int i2)
     return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// Exclusive prefix sum over the 256 threads of the block.
+// Exclusive prefix sum of v over the block's threads (up to 16 wavefronts).
 __device__ int block_exclusive_scan(int v, int* wsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int incl = v;
@@ -110,10 +169,11 @@ __device__ void scatter_chunk(const int* ids_lds, int npairs, int pair_base,
     const int nseg = (npairs + 63) / 64;
     for (int i = threadIdx.x; i < nseg * kMaxE; i += blockDim.x) seg_base[i] = 0;
     __syncthreads();
+    const int nwaves = blockDim.x >> 6;
     int my_e[2], my_rank[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const int g = wave + 4 * r;
+        const int g = wave + nwaves * r;
         my_e[r] = kMaxE;
         my_rank[r] = 0;
         if (g < nseg) {
@@ -144,7 +204,7 @@ __device__ void scatter_chunk(const int* ids_lds, int npairs, int pair_base,
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const int g = wave + 4 * r;
+        const int g = wave + nwaves * r;
         if (g < nseg && my_e[r] < kMaxE) {
             const int idx = g * 64 + lane;
             const int dest = seg_base[g * kMaxE + my_e[r]] + my_rank[r];
@@ -154,92 +214,131 @@ __device__ void scatter_chunk(const int* ids_lds, int npairs, int pair_base,
     }
 }
 
+// Top-k, softmax over the selected logits and the chunk histogram.  One
+// wavefront per token; a wavefront first loads the logits of up to 4 of its
+// tokens, then ranks them.  With a single chunk (kFused) the same block also
+// scans the histogram and scatters the pairs.
+// One step of a wave-wide argmax over (logit, id) pairs through the DPP
+// crossbar: combine with the lane the control selects (identity where there
+// is none).
+template <int kCtrl, int kRowMask, int kBankMask>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, -__builtin_inff()), __builtin_bit_cast(int, v), kCtrl, kRowMask,
+        kBankMask, false));
+    const int oi = __builtin_amdgcn_update_dpp(0x7FFFFFFF, i, kCtrl, kRowMask, kBankMask, false);
+    if (ranks_before(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Top-k of one token's logits held 4 per lane (expert lane + 64 q): k rounds
+// of a wave-wide argmax (larger logit, then lower id).  Each round reduces
+// within rows of 16 lanes (row shifts by 1, 2, 4, 8), then across rows (row
+// broadcasts of lanes 15 and 31), leaving the winner in lane 63.  After round
+// j, lane j keeps the j-th selection.
+__device__ __forceinline__ void wave_topk(float v0, float v1, float v2, float v3, int E, int k,
+                                       float& my_v, int& my_i) {
+    const int lane = threadIdx.x & 63;
+    float v[4] = {v0, v1, v2, v3};
+    my_v = 0.f;
+    my_i = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -__builtin_inff();
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + 64 * q;
+            if (e < E && ranks_before(v[q], e, bv, bi)) {
+                bv = v[q];
+                bi = e;
+            }
+        }
+        argmax_dpp<0x111, 0xF, 0xF>(bv, bi);   // row_shr:1
+        argmax_dpp<0x112, 0xF, 0xF>(bv, bi);   // row_shr:2
+        argmax_dpp<0x114, 0xF, 0xE>(bv, bi);   // row_shr:4
+        argmax_dpp<0x118, 0xF, 0xC>(bv, bi);   // row_shr:8
+        argmax_dpp<0x142, 0xA, 0xF>(bv, bi);   // row_bcast:15
+        argmax_dpp<0x143, 0xC, 0xF>(bv, bi);   // row_bcast:31
+        bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 63));
+        bi = __builtin_amdgcn_readlane(bi, 63);
+        if (bi >= E) bi = E - 1;              // only reachable with non-finite logits
+        if (lane == j) {
+            my_v = bv;
+            my_i = bi;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + 64 * q == bi) v[q] = -__builtin_inff();
+    }
+}
+
+// Top-k, softmax over the selected logits and the chunk histogram: one
+// wavefront per token (logit = the S router slices summed in order), the next
+// token's slices loaded while the current one is ranked.  With a single chunk
+// (kFused) the same block also scans the histogram and scatters the pairs.
 template <bool kFused>
-__global__ __launch_bounds__(256) void route_topk_kernel(
-    const float* __restrict__ partial, int splits, const float* __restrict__ br, int T,
-    int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts,
-    float* __restrict__ logits_out, int32_t* __restrict__ chunk_counts,
+__global__ __launch_bounds__(1024) void route_topk_kernel(
+    const float* __restrict__ P, int S, int T, int E, int k, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ chunk_counts,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
     __shared__ int cnt[kMaxE];
     __shared__ int chunk_ids[kChunkTokens * kMaxK];
     __shared__ int seg_base[8 * kMaxE];
     __shared__ int base_e[kMaxE];
-    __shared__ int wsum[4];
+    __shared__ int wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
     for (int i = tid; i < kMaxE; i += blockDim.x) cnt[i] = 0;
     __syncthreads();
     const int tbeg = blockIdx.x * kChunkTokens;
-    for (int tt = wave; tt < kChunkTokens; tt += 4) {
-        const int t = tbeg + tt;
-        if (t >= T) break;
-        float v[4];
+    const int ntok = T - tbeg < kChunkTokens ? T - tbeg : kChunkTokens;
+    constexpr int kMaxS = 16;
+    float nv[4][kMaxS];
+    auto load = [&](int tt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = lane + 64 * q;
-            v[q] = -FLT_MAX;
-            if (e < E) {
-                float s = 0.f;
-                for (int sp = 0; sp < splits; ++sp) s += partial[((int64_t)sp * T + t) * E + e];
-                if (br) s += br[e];
-                v[q] = s;
-                if (logits_out) logits_out[(int64_t)t * E + e] = s;
-            }
+            const bool ok = tt < ntok && e < E;
+#pragma unroll
+            for (int sp = 0; sp < kMaxS; ++sp)
+                nv[q][sp] = (ok && sp < S) ? P[((int64_t)sp * T + tbeg + tt) * E + e] : 0.f;
         }
-        bool taken[4] = {false, false, false, false};
-        float selv[kMaxK];
-        int seli[kMaxK];
+    };
+    load(wave);
+    for (int tt = wave; tt < ntok; tt += nwaves) {
+        float v[4];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            selv[j] = 0.f;
-            seli[j] = 0;
-            if (j < k) {
-                float bv = -FLT_MAX;
-                int bi = 0x7FFFFFFF;
+        for (int q = 0; q < 4; ++q) {
+            float acc = nv[q][0];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int e = lane + 64 * q;
-                    if (e < E && !taken[q] && ranks_before(v[q], e, bv, bi)) {
-                        bv = v[q];
-                        bi = e;
-                    }
-                }
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) {
-                    const float ov = __shfl_xor(bv, off);
-                    const int oi = __shfl_xor(bi, off);
-                    if (ranks_before(ov, oi, bv, bi)) {
-                        bv = ov;
-                        bi = oi;
-                    }
-                }
-                if (bi >= E) bi = E - 1;  // only reachable with non-finite logits
-                selv[j] = bv;
-                seli[j] = bi;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (lane + 64 * q == bi) taken[q] = true;
-            }
+            for (int sp = 1; sp < kMaxS; ++sp)
+                if (sp < S) acc += nv[q][sp];
+            v[q] = acc;
         }
-        // softmax over the selected logits (selv[0] is the largest)
-        float ex[kMaxK];
+        load(tt + nwaves);
+        const int t = tbeg + tt;
+        if (logits_out) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (lane + 64 * q < E) logits_out[(int64_t)t * E + lane + 64 * q] = v[q];
+        }
+        float my_v;
+        int my_i;
+        wave_topk(v[0], v[1], v[2], v[3], E, k, my_v, my_i);
+        // softmax over the k selected logits; lane 0 holds the largest
+        const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+        const float ex = lane < k ? expf(my_v - top) : 0.f;
         float den = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            ex[j] = 0.f;
-            if (j < k) {
-                ex[j] = expf(selv[j] - selv[0]);
-                den += ex[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k && lane == j) {
-                ids[(int64_t)t * k + j] = seli[j];
-                wts[(int64_t)t * k + j] = ex[j] / den;
-                atomicAdd(&cnt[seli[j]], 1);
-                chunk_ids[tt * k + j] = seli[j];
-            }
+        for (int j = 0; j < k; ++j)
+            den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+        if (lane < k) {
+            ids[(int64_t)t * k + lane] = my_i;
+            wts[(int64_t)t * k + lane] = ex / den;
+            atomicAdd(&cnt[my_i], 1);
+            chunk_ids[tt * k + lane] = my_i;
         }
     }
     __syncthreads();
@@ -258,14 +357,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
         if (tid == E - 1) offsets[E] = excl + c;
     }
     __syncthreads();
-    const int ntok = T - tbeg < kChunkTokens ? T - tbeg : kChunkTokens;
     scatter_chunk(chunk_ids, ntok * k, tbeg * k, base_e, E, seg_base, sorted, pos);
 }
 
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const int32_t* __restrict__ chunk_counts, int32_t* __restrict__ chunk_base, int chunks,
     int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-    __shared__ int wsum[4];
+    __shared__ int wsum[16];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
@@ -304,17 +402,19 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 RoutePlan plan_route(int T, int D, int E, int k) {
     RoutePlan p{};
     p.T = T; p.D = D; p.E = E; p.k = k;
-    const int tiles = ((T + kRouteTile - 1) / kRouteTile) * ((E + kRouteTile - 1) / kRouteTile);
-    int splits = 1024 / (tiles > 0 ? tiles : 1);
-    const int nch = D / 32;
-    if (splits > nch) splits = nch;
-    if (splits > 32) splits = 32;
-    if (splits < 1) splits = 1;
-    p.splits = splits;
+    p.token_tiles = T <= 64 ? 1 : 4;           // 16-token tiles per router block
+    const int tiles = ((E + 15) / 16) * ((T + 16 * p.token_tiles - 1) / (16 * p.token_tiles));
+    // split the contraction over blocks until ~128 blocks are busy (at most 16
+    // slices, and each wavefront keeps at least one 32-column step)
+    int S = (128 + tiles - 1) / tiles;
+    const int max_s = (D / 32) / kRouterWaves;
+    if (S > max_s) S = max_s;
+    if (S > 16) S = 16;
+    p.splits = S < 1 ? 1 : S;
     p.chunks = (T + kChunkTokens - 1) / kChunkTokens;
     size_t off = 0;
-    p.off_partial = off;
-    off = align256(off + (size_t)splits * T * E * sizeof(float));
+    p.off_logits = off;
+    off = align256(off + (size_t)p.splits * T * E * sizeof(float));
     p.off_chunk_counts = off;
     off = align256(off + (size_t)p.chunks * E * sizeof(int32_t));
     p.off_chunk_base = off;
@@ -328,20 +428,26 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
                         int32_t* sorted, int32_t* pos, float* logits_out, void* ws,
                         hipStream_t stream) {
     char* base = static_cast<char*>(ws);
-    float* partial = reinterpret_cast<float*>(base + p.off_partial);
+    float* P = reinterpret_cast<float*>(base + p.off_logits);
     int32_t* chunk_counts = reinterpret_cast<int32_t*>(base + p.off_chunk_counts);
     int32_t* chunk_base = reinterpret_cast<int32_t*>(base + p.off_chunk_base);
-    dim3 g1((p.T + kRouteTile - 1) / kRouteTile, (p.E + kRouteTile - 1) / kRouteTile, p.splits);
-    hipLaunchKernelGGL(router_partial_kernel, g1, dim3(256), 0, stream, x, wr, partial, p.T,
-                       p.D, p.E, p.splits);
-    if (p.chunks == 1) {
-        hipLaunchKernelGGL(route_topk_kernel<true>, dim3(1), dim3(256), 0, stream, partial,
-                           p.splits, br, p.T, p.E, p.k, ids, w, logits_out, chunk_counts,
-                           counts, offsets, sorted, pos);
+    if (p.token_tiles == 1) {
+        dim3 g((p.E + 15) / 16, (p.T + 15) / 16, p.splits);
+        hipLaunchKernelGGL(router_logits_kernel<1>, g, dim3(kRouterWaves * 64), 0, stream, x, wr,
+                           br, P, p.T, p.D, p.E, p.splits);
     } else {
-        hipLaunchKernelGGL(route_topk_kernel<false>, dim3(p.chunks), dim3(256), 0, stream,
-                           partial, p.splits, br, p.T, p.E, p.k, ids, w, logits_out,
-                           chunk_counts, counts, offsets, sorted, pos);
+        dim3 g((p.E + 15) / 16, (p.T + 63) / 64, p.splits);
+        hipLaunchKernelGGL(router_logits_kernel<4>, g, dim3(kRouterWaves * 64), 0, stream, x, wr,
+                           br, P, p.T, p.D, p.E, p.splits);
+    }
+    if (p.chunks == 1) {
+        hipLaunchKernelGGL(route_topk_kernel<true>, dim3(1), dim3(1024), 0, stream, P, p.splits,
+                           p.T, p.E, p.k, logits_out, ids, w, chunk_counts, counts, offsets,
+                           sorted, pos);
+    } else {
+        hipLaunchKernelGGL(route_topk_kernel<false>, dim3(p.chunks), dim3(256), 0, stream, P,
+                           p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts, counts,
+                           offsets, sorted, pos);
         hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, stream, chunk_counts,
                            chunk_base, p.chunks, p.E, counts, offsets);
         hipLaunchKernelGGL(route_scatter_kernel, dim3(p.chunks), dim3(256), 0, stream, ids,
