@@ -216,43 +216,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 
 constexpr int kStreamWaves = 8;
 constexpr int kNB = 4;                 // super-steps per load batch
-
-struct UnitTable {
-    int* units_before;                 // [E + 1] in LDS
-    int total;                         // number of units
-};
-
-// units_before[e] = sum over e' < e of ceil(n_e' / 16); needs >= 256 threads.
-__device__ void build_unit_table(const int32_t* __restrict__ offsets, int E, int* ub, int* wsum) {
-    const int tid = threadIdx.x;
-    int v = 0;
-    if (tid < E) v = (offsets[tid + 1] - offsets[tid] + 15) >> 4;
-    const int lane = tid & 63, wave = tid >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int n = __shfl_up(incl, off);
-        if (lane >= off) incl += n;
-    }
-    if (wave < 4 && lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    if (tid < 256) {
-        int base = 0;
-        for (int w = 0; w < wave; ++w) base += wsum[w];
-        if (tid < E) ub[tid] = base + incl - v;
-        if (tid == E - 1) ub[E] = base + incl;
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ int unit_expert(const int* ub, int E, int u) {
-    int lo = 0, hi = E - 1;            // largest e with ub[e] <= u
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (ub[mid] <= u) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
+constexpr int kMaxWaveTiles = 4;       // tiles a wavefront owns (outputs held in registers)
 
 // Staged activations.  The weights enter the matrix cores exactly as stored
 // (E2M1 codes + E8M0 block scales, v_mfma_scale_f32_16x16x128_f8f6f4 with an
@@ -298,26 +262,29 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
     if (threadIdx.x < 16)
         s_row[threadIdx.x] = threadIdx.x < nvalid
             ? (kGather ? sorted[row0 + threadIdx.x] / k : row0 + threadIdx.x) : -1;
-    __syncthreads();
     const int nblk = K / 32, nss = (nblk + 3) / 4;
     uint8_t* scales = lds + (size_t)nss * NT * 64 * 32;
+    // padding: rows past nvalid (all their blocks) and blocks past K -> zeros, scale 2^0
     for (int task = threadIdx.x; task < 16 * nss * 4; task += blockDim.x) {
-        const int m = task & 15, blk = task >> 4;         // blk < 4 * nss
-        const int ss = blk >> 2, gq = blk & 3;             // block gq of super-step ss
-        const bool live = blk < nblk && s_row[m] >= 0;
-        if (!live) {                                   // padding row or block: zeros, scale 2^0
-            const u32x4_t z = {0u, 0u, 0u, 0u};
+        const int m = task & 15, blk = task >> 4;
+        if (m < nvalid && blk < nblk) continue;
+        const int ss = blk >> 2, gq = blk & 3;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
+        for (int t = 0; t < NT; ++t) {
+            uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
-                    *reinterpret_cast<u32x4_t*>(base + (16 * (2 * (gq & 1) + half) + m) * 32 +
-                                                16 * (gq >> 1)) = z;
-                scales[(ss * NT + t) * 64 + gq * 16 + m] = 127;
-            }
-            continue;
+            for (int half = 0; half < 2; ++half)
+                *reinterpret_cast<u32x4_t*>(base + (16 * (2 * (gq & 1) + half) + m) * 32 +
+                                            16 * (gq >> 1)) = z;
+            scales[(ss * NT + t) * 64 + gq * 16 + m] = 127;
         }
+    }
+    __syncthreads();
+    // live (row, block) pairs only
+    for (int task = threadIdx.x; task < nvalid * nblk; task += blockDim.x) {
+        const int m = task % nvalid, blk = task / nvalid;
+        const int ss = blk >> 2, gq = blk & 3;
         float v[32];
         {
             const uint16_t* p = src + (int64_t)s_row[m] * K + blk * 32;
@@ -460,26 +427,27 @@ __device__ __forceinline__ void compute_batch(const WBatch<NS>& B, int ss0, int 
 // kGateUp: A = [gate rows; up rows] of W13 (NS = 2), B = x rows (2 fp8 terms),
 //          epilogue h = silu(g) * u -> fp16.
 // else:    A = W2 rows (NS = 1), B = h rows (3 fp8 terms), epilogue y -> fp32.
+//
+// Block b streams a fixed range of 16-row tiles of expert b / bpe, so its
+// first weight and scale loads are issued at entry, before the routing is
+// read.  The expert's pairs are taken 16 at a time (one pass over the tiles
+// per group of 16; decode steps have one group); blocks of experts without
+// pairs exit after their first prefetch.
 template <bool kGateUp>
 __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted, int D, int F, int E, int k,
+    const int32_t* __restrict__ sorted, int D, int F, int E, int k, int bpe,
     void* __restrict__ out) {
     constexpr int NS = kGateUp ? 2 : 1;
     constexpr int NT = kGateUp ? 2 : 3;
     extern __shared__ __align__(16) uint8_t lds_stage[];
-    __shared__ int ub[257];
-    __shared__ int wsum[4];
     __shared__ int s_row[16];
-    build_unit_table(offsets, E, ub, wsum);
     const int K = kGateUp ? D : F;           // contraction length
     const int NOUT = kGateUp ? F : D;        // output features (per stream)
     const int ntiles = NOUT / 16;
-    const int64_t total = (int64_t)ub[E] * ntiles;
-    const int64_t t_beg = total * blockIdx.x / gridDim.x;
-    const int64_t t_end = total * (blockIdx.x + 1) / gridDim.x;
-    if (t_beg >= t_end) return;
+    const int e = blockIdx.x / bpe, part = blockIdx.x - e * bpe;
+    const int a = (int)((int64_t)ntiles * part / bpe), b = (int)((int64_t)ntiles * (part + 1) / bpe);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -488,66 +456,87 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const uint8_t* lds_scales = lds_stage + (size_t)nss * NT * 64 * 32;
     uint8_t* wave_sc = lds_stage + (size_t)nss * NT * 64 * 33 + (size_t)wave * NS * 16 * nblk;
     const uint8_t* wsc = wave_sc + m * nblk;        // this lane's row of the committed run
+    const int my_tiles = a + wave < b ? (b - a - wave + kStreamWaves - 1) / kStreamWaves : 0;
+    const int steps = my_tiles * nbt;
+    const uint8_t* qe = wq + (size_t)e * (kGateUp ? 2 * F : D) * rowbytes;
+    const uint8_t* se = ws + (size_t)e * (kGateUp ? 2 * F : D) * nblk;
 
-    for (int64_t seg = t_beg; seg < t_end;) {
-        const int u = (int)(seg / ntiles);
-        const int64_t seg_end = min(t_end, (int64_t)(u + 1) * ntiles);
-        const int e = unit_expert(ub, E, u);
-        const int tg = u - ub[e];
-        const int row0 = offsets[e] + tg * 16;
-        const int nvalid = min(16, offsets[e + 1] - row0);
-        const int a = (int)(seg - (int64_t)u * ntiles), b = (int)(seg_end - (int64_t)u * ntiles);
-        const int my_tiles = a + wave < b ? (b - a - wave + kStreamWaves - 1) / kStreamWaves : 0;
-        const int steps = my_tiles * nbt;
-        const uint8_t* qe = wq + (size_t)e * (kGateUp ? 2 * F : D) * rowbytes;
-        const uint8_t* se = ws + (size_t)e * (kGateUp ? 2 * F : D) * nblk;
+    auto rows_of = [&](int s, const uint8_t* (&q)[NS]) {
+        const int tile = a + wave + (s / nbt) * kStreamWaves;
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+            const int row = r * F + tile * 16 + m;     // up rows follow the F gate rows
+            q[r] = qe + (size_t)row * rowbytes;
+        }
+    };
+    auto runs_of = [&](int tile, const uint8_t* (&run)[NS]) {
+#pragma unroll
+        for (int r = 0; r < NS; ++r) run[r] = se + (size_t)(r * F + tile * 16) * nblk;
+    };
+    // Ring of weight batches.  Prefetches are unconditional (steps past
+    // the end reload the last step's lines, which are cache hits) so the
+    // compiler never has to drain the load queue at a branch; only the
+    // compute is predicated.
+    const int last = steps > 0 ? steps - 1 : 0;
+    auto fetch = [&](WBatch<NS>& W, int s) {
+        const int sc_ = s < last ? s : last;
+        const uint8_t* q[NS];
+        rows_of(sc_, q);
+        load_batch<NS>(W, q, (sc_ % nbt) * kNB, g, nblk);
+    };
+    // ring depth: three batches for down (one weight stream), two for gate/up
+    // (two streams; a third would not fit the register file)
+    constexpr int kRing = kGateUp ? 2 : 3;
+    WBatch<NS> B0, B1, B2;
+    ScaleRegs<NS> SR;
+    auto prologue = [&]() {
+        if (steps > 0) {
+            const uint8_t* run[NS];
+            runs_of(a + wave, run);
+            fetch_scales<NS>(SR, run, lane, nblk);
+            fetch(B0, 0);
+            fetch(B1, 1);
+            if constexpr (kRing == 3) fetch(B2, 2);
+        }
+    };
+    prologue();                                // weights in flight before routing is read
+    const int row_beg = offsets[e], ne = offsets[e + 1] - row_beg;
+    if (ne <= 0) return;
 
-        auto rows_of = [&](int s, const uint8_t* (&q)[NS]) {
-            const int tile = a + wave + (s / nbt) * kStreamWaves;
-#pragma unroll
-            for (int r = 0; r < NS; ++r) {
-                const int row = r * F + tile * 16 + m;     // up rows follow the F gate rows
-                q[r] = qe + (size_t)row * rowbytes;
-            }
-        };
-        auto runs_of = [&](int tile, const uint8_t* (&run)[NS]) {
-#pragma unroll
-            for (int r = 0; r < NS; ++r) run[r] = se + (size_t)(r * F + tile * 16) * nblk;
-        };
-        auto epilogue = [&](int s, f32x4_t (&acc)[NS]) {
-            const int tile = a + wave + (s / nbt) * kStreamWaves;
-            if (m < nvalid) {
-                if constexpr (kGateUp) {
-                    typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
-                    f16x4_t hv;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) hv[q] = (_Float16)(silu_f32(acc[0][q]) * acc[1][q]);
-                    *reinterpret_cast<f16x4_t*>(static_cast<_Float16*>(out) +
-                                                (size_t)(row0 + m) * F + tile * 16 + 4 * g) = hv;
-                } else {
-                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) +
-                                                (size_t)(row0 + m) * D + tile * 16 + 4 * g) = acc[0];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        };
+    for (int tg = 0; tg < ne; tg += 16) {
+        const int row0 = row_beg + tg;
+        const int nvalid = min(16, ne - tg);
+        if (tg > 0) {
+            __syncthreads();                   // previous group's rows no longer read
+            prologue();
+        }
+        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row);
+        __syncthreads();
 
         f32x4_t acc[NS];
 #pragma unroll
         for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // Ring of three weight batches.  Prefetches are unconditional (steps past
-        // the end reload the last step's lines, which are cache hits) so the
-        // compiler never has to drain the load queue at a branch; only the
-        // compute is predicated.
-        const int last = steps > 0 ? steps - 1 : 0;
-        auto fetch = [&](WBatch<NS>& W, int s) {
-            const int sc_ = s < last ? s : last;
-            const uint8_t* q[NS];
-            rows_of(sc_, q);
-            load_batch<NS>(W, q, (sc_ % nbt) * kNB, g, nblk);
+        // Tile results stay in registers until the wave has issued its last
+        // load: on gfx9 the vector memory counter also covers stores, so an
+        // early store would make later load waits wait for its write too.
+        typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
+        typedef typename std::conditional<kGateUp, f16x4_t, f32x4_t>::type OutT;
+        OutT obuf[kMaxWaveTiles];
+        auto epilogue = [&](int s) {
+            const int j = s / nbt;
+            OutT res;
+            if constexpr (kGateUp) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) res[q] = (_Float16)(silu_f32(acc[0][q]) * acc[1][q]);
+            } else {
+                res = acc[0];
+            }
+#pragma unroll
+            for (int jj = 0; jj < kMaxWaveTiles; ++jj)
+                if (jj == j) obuf[jj] = res;
+#pragma unroll
+            for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         };
-        ScaleRegs<NS> SR;
         auto consume = [&](const WBatch<NS>& W, int s) {
             if (s % nbt == 0) {               // tile switch: commit its scales, fetch the next's
                 commit_scales<NS>(SR, wave_sc, lane, nblk);
@@ -558,29 +547,32 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
             }
             compute_batch<NS, NT>(W, (s % nbt) * kNB, nss, lds_stage, lds_scales, wsc, lane, g,
                                   nblk, acc);
-            if (s % nbt == nbt - 1) epilogue(s, acc);
+            if (s % nbt == nbt - 1) epilogue(s);
         };
-        WBatch<NS> B0, B1, B2;
-        if (steps > 0) {          // first weights in flight while the activations are staged
-            const uint8_t* run[NS];
-            runs_of(a + wave, run);
-            fetch_scales<NS>(SR, run, lane, nblk);
-            fetch(B0, 0);
-            fetch(B1, 1);
-            fetch(B2, 2);
-        }
-        __syncthreads();                       // previous unit's rows no longer read
-        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row);
-        __syncthreads();
-        for (int s = 0; s < steps; s += 3) {
+        for (int s = 0; s < steps; s += kRing) {
             consume(B0, s);
-            fetch(B0, s + 3);
+            fetch(B0, s + kRing);
             if (s + 1 < steps) consume(B1, s + 1);
-            fetch(B1, s + 4);
-            if (s + 2 < steps) consume(B2, s + 2);
-            fetch(B2, s + 5);
+            fetch(B1, s + 1 + kRing);
+            if constexpr (kRing == 3) {
+                if (s + 2 < steps) consume(B2, s + 2);
+                fetch(B2, s + 5);
+            }
         }
-        seg = seg_end;
+        if (m < nvalid) {
+#pragma unroll
+            for (int jj = 0; jj < kMaxWaveTiles; ++jj) {
+                if (jj < my_tiles) {
+                    const int tile = a + wave + jj * kStreamWaves;
+                    if constexpr (kGateUp)
+                        *reinterpret_cast<OutT*>(static_cast<_Float16*>(out) + (size_t)(row0 + m) * F +
+                                                 tile * 16 + 4 * g) = obuf[jj];
+                    else
+                        *reinterpret_cast<OutT*>(static_cast<float*>(out) + (size_t)(row0 + m) * D +
+                                                 tile * 16 + 4 * g) = obuf[jj];
+                }
+            }
+        }
     }
 }
 
@@ -628,13 +620,17 @@ static size_t stream_lds_bytes(int K, int NT, int NS) {
     return (size_t)((K / 32 + 3) / 4) * NT * 64 * 33 + (size_t)kStreamWaves * NS * 16 * (K / 32);
 }
 
-// One round of blocks over the 256 CUs of MI355X (two blocks per CU when the
-// staged rows leave room for two), never more than one block per 8 tiles.
-static int stream_grid(int64_t tiles_upper, size_t lds_bytes) {
-    const int per_cu = lds_bytes * 2 <= kMaxStreamLds ? 2 : 1;
-    int64_t g = (tiles_upper + kStreamWaves - 1) / kStreamWaves;
-    if (g > 256 * per_cu) g = 256 * per_cu;
-    return (int)(g < 1 ? 1 : g);
+// Blocks per expert for the streaming kernels: about 256 blocks in all (one
+// per CU of MI355X) and at least 2 per expert, so untouched experts' CUs are
+// reused by the dispatcher; at least 8 tiles (one per wavefront) per block
+// where possible, and never more than kMaxWaveTiles per wavefront.
+static int stream_blocks_per_expert(int E, int ntiles) {
+    int bpe = (256 + E - 1) / E;
+    if (bpe < 2) bpe = 2;
+    if (bpe > ntiles / kStreamWaves) bpe = ntiles / kStreamWaves;
+    const int min_bpe = (ntiles + kStreamWaves * kMaxWaveTiles - 1) / (kStreamWaves * kMaxWaveTiles);
+    if (bpe < min_bpe) bpe = min_bpe;
+    return bpe < 1 ? 1 : bpe;
 }
 
 static int blocks_per_expert(int E, int ntiles) {
@@ -655,24 +651,24 @@ hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
         const hipError_t er = hipEventRecord(events[0], stream);
         if (er != hipSuccess) return er;
     }
-    const int64_t P = (int64_t)p.T * p.k;
-    const int64_t units_max = std::min<int64_t>(P, (P + 15) / 16 + p.E);
     const size_t lds_gu = stream_lds_bytes(p.D, 2, 2), lds_dn = stream_lds_bytes(p.F, 3, 1);
     if (lds_gu <= kMaxStreamLds && lds_dn <= kMaxStreamLds && p.D <= 4096 && p.F <= 4096) {
-        const int g1 = stream_grid(units_max * (p.F / 16), lds_gu);
+        const int bpe1 = stream_blocks_per_expert(p.E, p.F / 16);
+        const int g1 = p.E * bpe1;
         if (lds_gu > 65536) {
             hipError_t er = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<true>),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu);
             if (er != hipSuccess) return er;
         }
         hipLaunchKernelGGL(expert_stream_kernel<true>, dim3(g1), dim3(kStreamWaves * 64), lds_gu,
-                           stream, x, w13q, w13s, offsets, sorted, p.D, p.F, p.E, p.k,
+                           stream, x, w13q, w13s, offsets, sorted, p.D, p.F, p.E, p.k, bpe1,
                            static_cast<void*>(h));
         if (events) {
             const hipError_t er = hipEventRecord(events[1], stream);
             if (er != hipSuccess) return er;
         }
-        const int g2 = stream_grid(units_max * (p.D / 16), lds_dn);
+        const int bpe2 = stream_blocks_per_expert(p.E, p.D / 16);
+        const int g2 = p.E * bpe2;
         if (lds_dn > 65536) {
             hipError_t er = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<false>),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn);
@@ -680,7 +676,7 @@ hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
         }
         hipLaunchKernelGGL(expert_stream_kernel<false>, dim3(g2), dim3(kStreamWaves * 64), lds_dn,
                            stream, reinterpret_cast<const uint16_t*>(h), w2q, w2s, offsets, sorted,
-                           p.D, p.F, p.E, p.k, static_cast<void*>(y));
+                           p.D, p.F, p.E, p.k, bpe2, static_cast<void*>(y));
     } else {
         const int bpe1 = blocks_per_expert(p.E, p.F / 16);
         hipLaunchKernelGGL(gateup_stream_kernel, dim3(p.E * bpe1), dim3(256), 0, stream, x, w13q,

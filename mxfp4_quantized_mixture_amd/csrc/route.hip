@@ -9,13 +9,12 @@
 //
 // Kernels:
 //   router_logits_kernel   matrix-core logits (fp32 weights as 3 exact bf16
-//                          terms), split-K over 16 wavefronts
+//                          terms), split-K over wavefronts and blocks
 //   route_topk_kernel      one wavefront per token: k rounds of wave-wide
-//                          argmax, softmax over the k, LDS histogram
-//                          per 64-token chunk; with a single chunk it also runs
-//                          the scan and the scatter (one launch for decode)
-//   route_scan_kernel      per-expert running sums over chunks + block scan
-//   route_scatter_kernel   stable scatter: ranks from wavefront ballots
+//                          DPP argmax, softmax over the k, per-chunk histogram
+//   route_finish_kernel    few pairs: histogram, scan and scatter in one block
+//   route_scan_kernel      many pairs: per-expert running sums over chunks
+//   route_scatter_kernel   many pairs: stable scatter, ranks from ballots
 // Nothing uses floating-point atomics, so results are deterministic.
 #include <float.h>
 
@@ -24,7 +23,8 @@
 
 namespace moe {
 
-constexpr int kChunkTokens = 64;   // tokens per top-k / histogram chunk
+constexpr int kChunkTokens = 16;   // tokens per top-k / histogram chunk (one per wavefront)
+constexpr int kFinishMaxPairs = 512;  // pairs the single-block finish kernel handles
 constexpr int kMaxK = 8;
 constexpr int kMaxE = 256;
 
@@ -214,10 +214,6 @@ __device__ void scatter_chunk(const int* ids_lds, int npairs, int pair_base,
     }
 }
 
-// Top-k, softmax over the selected logits and the chunk histogram.  One
-// wavefront per token; a wavefront first loads the logits of up to 4 of its
-// tokens, then ranks them.  With a single chunk (kFused) the same block also
-// scans the histogram and scatters the pairs.
 // One step of a wave-wide argmax over (logit, id) pairs through the DPP
 // crossbar: combine with the lane the control selects (identity where there
 // is none).
@@ -275,51 +271,38 @@ __device__ __forceinline__ void wave_topk(float v0, float v1, float v2, float v3
 }
 
 // Top-k, softmax over the selected logits and the chunk histogram: one
-// wavefront per token (logit = the S router slices summed in order), the next
-// token's slices loaded while the current one is ranked.  With a single chunk
-// (kFused) the same block also scans the histogram and scatters the pairs.
-template <bool kFused>
-__global__ __launch_bounds__(1024) void route_topk_kernel(
+// wavefront per token of the block's 16-token chunk (logit = the S router
+// slices summed in order).
+__global__ __launch_bounds__(kChunkTokens * 64) void route_topk_kernel(
     const float* __restrict__ P, int S, int T, int E, int k, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ chunk_counts,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ chunk_counts) {
     __shared__ int cnt[kMaxE];
-    __shared__ int chunk_ids[kChunkTokens * kMaxK];
-    __shared__ int seg_base[8 * kMaxE];
-    __shared__ int base_e[kMaxE];
-    __shared__ int wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
     for (int i = tid; i < kMaxE; i += blockDim.x) cnt[i] = 0;
-    __syncthreads();
-    const int tbeg = blockIdx.x * kChunkTokens;
-    const int ntok = T - tbeg < kChunkTokens ? T - tbeg : kChunkTokens;
+    const int t = blockIdx.x * kChunkTokens + wave;
     constexpr int kMaxS = 16;
-    float nv[4][kMaxS];
-    auto load = [&](int tt) {
+    float v[4];
+    {
+        float part[4][kMaxS];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = lane + 64 * q;
-            const bool ok = tt < ntok && e < E;
+            const bool ok = t < T && e < E;
 #pragma unroll
             for (int sp = 0; sp < kMaxS; ++sp)
-                nv[q][sp] = (ok && sp < S) ? P[((int64_t)sp * T + tbeg + tt) * E + e] : 0.f;
+                part[q][sp] = (ok && sp < S) ? P[((int64_t)sp * T + t) * E + e] : 0.f;
         }
-    };
-    load(wave);
-    for (int tt = wave; tt < ntok; tt += nwaves) {
-        float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            float acc = nv[q][0];
+            float acc = part[q][0];
 #pragma unroll
             for (int sp = 1; sp < kMaxS; ++sp)
-                if (sp < S) acc += nv[q][sp];
+                if (sp < S) acc += part[q][sp];
             v[q] = acc;
         }
-        load(tt + nwaves);
-        const int t = tbeg + tt;
+    }
+    __syncthreads();                           // cnt cleared
+    if (t < T) {
         if (logits_out) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -338,16 +321,31 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(
             ids[(int64_t)t * k + lane] = my_i;
             wts[(int64_t)t * k + lane] = ex / den;
             atomicAdd(&cnt[my_i], 1);
-            chunk_ids[tt * k + lane] = my_i;
         }
     }
     __syncthreads();
-    if (!kFused) {
-        for (int e = tid; e < E; e += blockDim.x)
-            chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
-        return;
+    for (int e = tid; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Few pairs (P <= kFinishMaxPairs): one block rebuilds the histogram from the
+// ids, scans it and scatters every pair.
+__global__ __launch_bounds__(1024) void route_finish_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
+    __shared__ int cnt[kMaxE];
+    __shared__ int pair_e[kFinishMaxPairs];
+    __shared__ int seg_base[8 * kMaxE];
+    __shared__ int base_e[kMaxE];
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kMaxE; i += blockDim.x) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = ids[p];
+        pair_e[p] = e;
+        atomicAdd(&cnt[e], 1);
     }
-    // Single chunk: the chunk's histogram is the whole histogram.
+    __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
     const int excl = block_exclusive_scan(c, wsum);
     if (tid < E) {
@@ -357,7 +355,7 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(
         if (tid == E - 1) offsets[E] = excl + c;
     }
     __syncthreads();
-    scatter_chunk(chunk_ids, ntok * k, tbeg * k, base_e, E, seg_base, sorted, pos);
+    scatter_chunk(pair_e, P, 0, base_e, E, seg_base, sorted, pos);
 }
 
 __global__ __launch_bounds__(256) void route_scan_kernel(
@@ -440,14 +438,13 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
         hipLaunchKernelGGL(router_logits_kernel<4>, g, dim3(kRouterWaves * 64), 0, stream, x, wr,
                            br, P, p.T, p.D, p.E, p.splits);
     }
-    if (p.chunks == 1) {
-        hipLaunchKernelGGL(route_topk_kernel<true>, dim3(1), dim3(1024), 0, stream, P, p.splits,
-                           p.T, p.E, p.k, logits_out, ids, w, chunk_counts, counts, offsets,
-                           sorted, pos);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(p.chunks), dim3(kChunkTokens * 64), 0, stream, P,
+                       p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts);
+    const int pairs = p.T * p.k;
+    if (pairs <= kFinishMaxPairs) {
+        hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, p.E,
+                           counts, offsets, sorted, pos);
     } else {
-        hipLaunchKernelGGL(route_topk_kernel<false>, dim3(p.chunks), dim3(256), 0, stream, P,
-                           p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts, counts,
-                           offsets, sorted, pos);
         hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, stream, chunk_counts,
                            chunk_base, p.chunks, p.E, counts, offsets);
         hipLaunchKernelGGL(route_scatter_kernel, dim3(p.chunks), dim3(256), 0, stream, ids,
