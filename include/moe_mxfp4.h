@@ -55,7 +55,7 @@ typedef enum {
     MOE_ERR_NULL = 1,       /* a required pointer is NULL */
     MOE_ERR_SHAPE = 2,      /* a size is out of range or not a multiple of 32 */
     MOE_ERR_WORKSPACE = 3,  /* workspace NULL or smaller than *_workspace_size */
-    MOE_ERR_ENUM = 4,       /* unknown scale rule */
+    MOE_ERR_ENUM = 4,       /* unknown scale rule or expert-MLP algorithm */
     MOE_ERR_HIP = 5,        /* a kernel launch failed */
     MOE_ERR_ALIGN = 6       /* a pointer is not 16-byte aligned */
 } moe_status_t;
@@ -67,6 +67,17 @@ typedef enum {
                                    scales into [6, 12) and saturates to 6 */
     MXFP4_SCALE_OCP = 1         /* s = floor(log2(amax)) - 2 (OCP MX v1.0) */
 } mxfp4_scale_rule_t;
+
+/* How moe_expert_mlp_ex runs the experts (moe_expert_mlp: automatic). */
+typedef enum {
+    MOE_MLP_AUTO = 0,          /* grouped GEMM when D % 64 == 0, F % 64 == 0 and
+                                  T*k >= 32*E (32 pairs per expert on average),
+                                  weight streaming otherwise */
+    MOE_MLP_STREAM = 1,        /* weight streaming: each touched expert's weights
+                                  are read once per group of 16 of its pairs */
+    MOE_MLP_GROUPED_GEMM = 2   /* tiled grouped GEMM over 128-pair tiles; needs
+                                  D % 64 == 0 and F % 64 == 0 (else MOE_ERR_SHAPE) */
+} moe_mlp_algo_t;
 
 /* Human-readable name of a status code (static string). */
 MOE_API const char *moe_status_string(int status);
@@ -144,17 +155,23 @@ MOE_API moe_status_t moe_route(const uint16_t *x, const float *wr, const float *
  * For each routed pair p = t*k + j with expert e = the expert of p:
  *   g = Wg_e x_t, u = Wu_e x_t, h = silu(g) * u, y_p = W2_e h,
  *   out[t] = sum over j = 0..k-1 (in slot order) of topk_w[t, j] * y_p.
- * Arithmetic: gate/up on bf16 matrix cores with the weights widened exactly
- * to bf16 and fp32 accumulation; h rounded to fp16; down on fp16 matrix cores
- * with the weights widened exactly to fp16 (exact for scale bytes in
- * [104, 140], i.e. 2^-23..2^13; outside that window weights are rounded to
- * fp16); fp32 combine; output rounded to bf16.
+ * Arithmetic: the weights enter the gfx950 block-scaled matrix-core product
+ * as stored (E2M1 codes, with their E8M0 block scales as the hardware scale
+ * operand); the activations enter it as fp8 (E4M3) residual terms, each with
+ * its own E8M0 scale per 32-element block: x as 2 terms (exact for bf16), h
+ * as 3 terms (h rounded to fp16 first on the weight-streaming path, split
+ * from fp32 on the grouped-GEMM path); fp32 accumulation and combine; output
+ * rounded to bf16.  (With D or F above 4096 the streaming path widens the
+ * weights instead: to bf16 for gate/up, exactly, and to fp16 for down, exact
+ * for scale bytes in [104, 140].)
  * Preconditions: as moe_route, plus 32 <= F, F % 32 == 0, the routing arrays
  * consistent with each other (as moe_route writes them).
  * stage_events: NULL, or 4 events recorded on `stream` before the gate/up
  * kernel, after it, after the down kernel and after the combine kernel.
  * Errors: MOE_ERR_SHAPE, MOE_ERR_NULL, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN,
- * MOE_ERR_HIP.
+ * MOE_ERR_HIP.  The workspace size covers both algorithms.
+ * moe_expert_mlp_ex: the same with the algorithm chosen by the caller
+ * (moe_mlp_algo_t); MOE_ERR_ENUM for an unknown value.
  */
 MOE_API size_t moe_expert_mlp_workspace_size(int32_t T, int32_t D, int32_t F,
                                      int32_t E, int32_t k);
@@ -166,6 +183,15 @@ MOE_API moe_status_t moe_expert_mlp(const uint16_t *x, const uint8_t *w13_q,
                             const int32_t *pair_pos, int32_t T, int32_t D,
                             int32_t F, int32_t E, int32_t k, uint16_t *out,
                             void *ws, size_t ws_bytes,
+                            hipEvent_t *stage_events, hipStream_t stream);
+MOE_API moe_status_t moe_expert_mlp_ex(const uint16_t *x, const uint8_t *w13_q,
+                            const uint8_t *w13_s, const uint8_t *w2_q,
+                            const uint8_t *w2_s, const float *topk_w,
+                            const int32_t *offsets,
+                            const int32_t *sorted_pairs,
+                            const int32_t *pair_pos, int32_t T, int32_t D,
+                            int32_t F, int32_t E, int32_t k, uint16_t *out,
+                            void *ws, size_t ws_bytes, int algo,
                             hipEvent_t *stage_events, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -10,7 +10,8 @@ Functions mirror the C entry points:
     mxfp4_quantize(w, rule)           -> (q, s)
     mxfp4_dequantize(q, s)            -> bf16 tensor
     moe_route(x, wr, br, k)           -> Routing
-    moe_expert_mlp(x, weights, routing) -> bf16 [T, D]
+    moe_expert_mlp(x, weights, routing, algo=MLP_AUTO) -> bf16 [T, D]
+      (moe_expert_mlp_ex in the C ABI when an algorithm is named)
 and MoELayer bundles quantized weights and workspaces for repeated calls.
 """
 
@@ -24,11 +25,13 @@ import torch
 
 __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "moe_route", "moe_expert_mlp",
            "Routing", "ExpertWeights", "MoELayer", "MoEError", "lib",
-           "SCALE_FLOOR_DIV6", "SCALE_OCP", "LIB_PATH"]
+           "SCALE_FLOOR_DIV6", "SCALE_OCP", "MLP_AUTO", "MLP_STREAM", "MLP_GROUPED_GEMM",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
 SCALE_FLOOR_DIV6 = 0
 SCALE_OCP = 1
+MLP_AUTO, MLP_STREAM, MLP_GROUPED_GEMM = 0, 1, 2
 
 
 class MoEError(RuntimeError):
@@ -68,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_mlp.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                      P, P, sz, P, P]
         L.moe_expert_mlp.restype = ctypes.c_int
+        L.moe_expert_mlp_ex.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                        P, P, sz, ctypes.c_int, P, P]
+        L.moe_expert_mlp_ex.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -212,7 +218,7 @@ def mlp_workspace(T: int, D: int, F: int, E: int, k: int, device) -> torch.Tenso
 
 def moe_expert_mlp(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
                    out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                   events=None) -> torch.Tensor:
+                   events=None, algo: int = MLP_AUTO) -> torch.Tensor:
     T, D = x.shape
     E, F = weights.E, weights.F
     k = routing.ids.shape[1]
@@ -221,14 +227,15 @@ def moe_expert_mlp(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
     out = out if out is not None else torch.empty(T, D, dtype=torch.bfloat16, device=x.device)
     ws = ws if ws is not None else mlp_workspace(T, D, F, E, k, x.device)
     ev = None if events is None else _event_array(events)
-    _check("moe_expert_mlp", lib().moe_expert_mlp(
+    _check("moe_expert_mlp", lib().moe_expert_mlp_ex(
         _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
         _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
         _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w", torch.float32),
         _dev(routing.offsets, "offsets", torch.int32),
         _dev(routing.sorted_pairs, "sorted_pairs", torch.int32),
         _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
-        _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), ev, _stream(x.device)))
+        _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), algo, ev,
+        _stream(x.device)))
     return out
 
 
@@ -263,7 +270,8 @@ class PreparedLayer:
 
     def __init__(self, x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None,
                  weights: ExpertWeights, k: int, out: torch.Tensor, routing: Routing,
-                 route_ws: torch.Tensor, mlp_ws: torch.Tensor, stream=None):
+                 route_ws: torch.Tensor, mlp_ws: torch.Tensor, stream=None,
+                 algo: int = MLP_AUTO):
         T, D = x.shape
         E, F = weights.E, weights.F
         self.L = lib()
@@ -282,7 +290,7 @@ class PreparedLayer:
             _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w"),
             _dev(routing.offsets, "offsets"), _dev(routing.sorted_pairs, "sorted_pairs"),
             _dev(routing.pair_pos, "pair_pos"), T, D, F, E, k, _dev(out, "out", torch.bfloat16),
-            _dev(mlp_ws, "ws"), mlp_ws.numel())
+            _dev(mlp_ws, "ws"), mlp_ws.numel(), algo)
         self.stream = st
 
     @staticmethod
@@ -293,6 +301,6 @@ class PreparedLayer:
         s = self.L.moe_route(*self.route_args)
         if s:
             raise MoEError("moe_route", s)
-        s = self.L.moe_expert_mlp(*self.mlp_head, event_array, self.stream)
+        s = self.L.moe_expert_mlp_ex(*self.mlp_head, event_array, self.stream)
         if s:
             raise MoEError("moe_expert_mlp", s)

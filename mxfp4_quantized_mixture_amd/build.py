@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["quantize.hip", "route.hip", "expert_mlp.hip", "api.hip"]
+SOURCES = ["quantize.hip", "route.hip", "expert_mlp.hip", "expert_gemm.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

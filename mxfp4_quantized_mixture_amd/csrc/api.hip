@@ -26,7 +26,7 @@ const char* moe_status_string(int status) {
         case MOE_ERR_NULL: return "a required pointer is NULL";
         case MOE_ERR_SHAPE: return "a size is out of range or not a multiple of 32";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
-        case MOE_ERR_ENUM: return "unknown scale rule";
+        case MOE_ERR_ENUM: return "unknown scale rule or algorithm";
         case MOE_ERR_HIP: return "kernel launch failed";
         case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         default: return "unknown status";
@@ -85,7 +85,21 @@ moe_status_t moe_expert_mlp(const uint16_t* x, const uint8_t* w13_q, const uint8
                             const int32_t* pair_pos, int32_t T, int32_t D, int32_t F,
                             int32_t E, int32_t k, uint16_t* out, void* ws, size_t ws_bytes,
                             hipEvent_t* stage_events, hipStream_t stream) {
+    return moe_expert_mlp_ex(x, w13_q, w13_s, w2_q, w2_s, topk_w, offsets, sorted_pairs,
+                             pair_pos, T, D, F, E, k, out, ws, ws_bytes, MOE_MLP_AUTO,
+                             stage_events, stream);
+}
+
+moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                               const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_w,
+                               const int32_t* offsets, const int32_t* sorted_pairs,
+                               const int32_t* pair_pos, int32_t T, int32_t D, int32_t F,
+                               int32_t E, int32_t k, uint16_t* out, void* ws, size_t ws_bytes,
+                               int algo, hipEvent_t* stage_events, hipStream_t stream) {
+    if (algo != MOE_MLP_AUTO && algo != MOE_MLP_STREAM && algo != MOE_MLP_GROUPED_GEMM)
+        return MOE_ERR_ENUM;
     if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return MOE_ERR_SHAPE;
+    if (algo == MOE_MLP_GROUPED_GEMM && (D % 64 != 0 || F % 64 != 0)) return MOE_ERR_SHAPE;
     if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !offsets || !sorted_pairs ||
         !pair_pos || !out)
         return MOE_ERR_NULL;
@@ -94,7 +108,7 @@ moe_status_t moe_expert_mlp(const uint16_t* x, const uint8_t* w13_q, const uint8
     if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
         !aligned16(w2_s) || !aligned16(out) || !aligned16(ws))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_mlp(plan, x, w13_q, w13_s, w2_q, w2_s, topk_w, offsets,
+    return hip_status(moe::launch_mlp(plan, algo, x, w13_q, w13_s, w2_q, w2_s, topk_w, offsets,
                                       sorted_pairs, pair_pos, out, ws, stage_events, stream));
 }
 

@@ -1,0 +1,516 @@
+// expert_gemm.hip -- the expert MLP as two tiled grouped GEMMs, for batches in
+// which experts receive many tokens (prefill), gfx950.
+//
+// The layer is the one of the weight-streaming kernels ("Welcome GPT OSS",
+// section 4: SwiGLU experts; "Tricks", section 8: GEMMs that understand the
+// 32-element blocks and their scales).  For each expert e with token rows X_e
+// (its routed pairs in sorted order):  [G | U] = X_e W13_e^T,
+// H = silu(G) * U,  Y = H W2_e^T;  the weighted combine follows.
+//
+// Matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4.  The MXFP4 weights are its
+// A operand exactly as stored (E2M1 codes, E8M0 block scales as the hardware
+// scale operand); the activations are its B operand as fp8 (E4M3) residual
+// terms with their own E8M0 block scales: x (bf16) as 2 terms, which is exact,
+// and h as 3 terms, produced directly by the gate/up epilogue.
+//
+// Operand layouts of the 32x32x64 product (lane l, n = l % 32, g = l / 32):
+//   A: row n, K = 32 g .. 32 g + 31 (one MXFP4 block, low nibble first) in
+//      the first 16 bytes; scale = that block's E8M0 byte.
+//   B: column n, bytes 0..15 = K 16 g .. 16 g + 15, bytes 16..31 =
+//      K 32 + 16 g .. + 15; scale = K-block g of column n.
+//   C: element i = row 8 (i / 4) + 4 g + i % 4, column n.
+//
+// Activation term rows.  A row of K elements (K % 64 == 0) is S = K / 64
+// steps of term_chunk(NT) = NT * 64 + 16 bytes.  Term t's 64 codes sit at
+// 64 t in B operand order: [lane group 0: elements 0..15 of block 2s,
+// elements 0..15 of block 2s+1][lane group 1: elements 16..31 of block 2s,
+// 16..31 of block 2s+1]; byte NT * 64 + 2 t + h holds the E8M0 scale of term
+// t of block 2s + h (the rest of the last 16 bytes is padding).  Codes and
+// scales of a step travel together, so staging a step is one contiguous copy
+// per row.
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kGemmRows = 128;      // routed pairs per tile: 4 fragments of 32
+constexpr int kGemmThreads = 256;   // 4 wavefronts, one per SIMD
+constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
+
+__host__ __device__ constexpr int term_chunk(int NT) { return NT * 64 + 16; }
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
+template <int N, typename Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---------------------------------------------------------------------------
+// bf16 rows -> NT fp8 term rows.  One thread per (row, 64-element step).
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256) void split_terms_kernel(const uint16_t* __restrict__ src,
+                                                          int rows, int K,
+                                                          uint8_t* __restrict__ tq) {
+    const int S = K / 64;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)rows * S) return;
+    const int row = (int)(idx / S), s = (int)(idx - (int64_t)row * S);
+    const uint16_t* p = src + (size_t)row * K + (size_t)s * 64;
+    uint8_t* o = tq + ((size_t)row * S + s) * term_chunk(NT);
+    uint32_t sc_bytes[2] = {0u, 0u};
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(p + hb * 32 + c * 8);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[c * 8 + 2 * h] = bf16_to_f32(raw[h] & 0xFFFFu);
+                v[c * 8 + 2 * h + 1] = bf16_to_f32(raw[h] >> 16);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            const int se = fp8_term_exponent(amax);
+            const float inv = exp2i_neg(se), sc = exp2i(se);
+            uint32_t q[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                q[w] = pack4_fp8(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
+                                 v[4 * w + 3] * inv);
+            if (t + 1 < NT) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) sub4_fp8(v + 4 * w, q[w], sc);
+            }
+            *reinterpret_cast<u32x4_t*>(o + t * 64 + 16 * hb) = u32x4_t{q[0], q[1], q[2], q[3]};
+            *reinterpret_cast<u32x4_t*>(o + t * 64 + 32 + 16 * hb) = u32x4_t{q[4], q[5], q[6], q[7]};
+            const int byte = 2 * t + hb;
+            sc_bytes[byte >> 2] |= (uint32_t)(se + 127) << (8 * (byte & 3));
+        }
+    }
+    *reinterpret_cast<u32x4_t*>(o + NT * 64) = u32x4_t{sc_bytes[0], sc_bytes[1], 0u, 0u};
+}
+
+// ---------------------------------------------------------------------------
+// Tile table: expert e's pairs [offsets[e], offsets[e+1]) in tiles of
+// kGemmRows, experts in order.  tiles[2 i] = first sorted row of tile i,
+// tiles[2 i + 1] = e | rows << 16; tiles[2 max_tiles] = number of tiles.
+// One block of 256 threads (E <= 256).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                         int E, int max_tiles,
+                                                         int32_t* __restrict__ tiles) {
+    __shared__ int part[256];
+    const int e = threadIdx.x;
+    const int beg = e < E ? offsets[e] : 0;
+    const int ne = e < E ? offsets[e + 1] - beg : 0;
+    const int c = (ne + kGemmRows - 1) / kGemmRows;
+    part[e] = c;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {        // inclusive scan
+        const int v = e >= d ? part[e - d] : 0;
+        __syncthreads();
+        part[e] += v;
+        __syncthreads();
+    }
+    const int first = part[e] - c;
+    for (int j = 0; j < c && first + j < max_tiles; ++j) {
+        const int rows = min(kGemmRows, ne - j * kGemmRows);
+        tiles[2 * (first + j)] = beg + j * kGemmRows;
+        tiles[2 * (first + j) + 1] = e | (rows << 16);
+    }
+    if (e == 255) tiles[2 * max_tiles] = min(part[255], max_tiles);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM.  Block = one tile of kGemmRows pairs x one column range of
+// output fragments (32 outputs each).  Four wavefronts, each owning all 128
+// pairs (4 B fragments) and kWaveFrags output fragments:
+//   gate/up: 2 feature fragments -> 4 A fragments (their gate and up rows),
+//            epilogue h = silu(g) * u written as 3-term rows;
+//   down:    4 output fragments -> 4 A fragments, epilogue y (fp32).
+// The contraction runs in stages of kStage 64-wide steps (128 per stage
+// when LDS allows): activations go global -> registers -> one of two LDS
+// buffers, weights global -> registers, each a stage ahead, with one
+// barrier per stage.
+// ---------------------------------------------------------------------------
+template <bool kGateUp, int kStage>
+__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
+    const uint8_t* __restrict__ bq, const int32_t* __restrict__ sorted, int k,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
+    uint8_t* __restrict__ hq, float* __restrict__ y) {
+    constexpr int NT = kGateUp ? 2 : 3;                 // activation terms
+    constexpr int NA = 4;                               // A fragments per wave
+    constexpr int kWaveFrags = kGateUp ? 2 : 4;         // output fragments per wave
+    constexpr int kChunk = term_chunk(NT);
+    // LDS slot of one step: the 128 rows' step chunks, row-major.  The row
+    // pitch kChunk = 16 (NT * 4 + 1) bytes keeps both the staging copy and
+    // the operand reads (lanes n = 0..15 at 16-byte units 9 n or 13 n mod 16)
+    // free of bank conflicts.
+    constexpr int kSlotBytes = kGemmRows * kChunk;
+    constexpr int kRowPieces = kChunk / 16;
+    constexpr int kPieces = (kGemmRows * kRowPieces + kGemmThreads - 1) / kGemmThreads;
+    constexpr int kBufBytes = kStage * kSlotBytes;      // one stage of activation steps
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ int s_src[kGemmRows];
+
+    // Work item L = m-tile * ntl + column tile.  The dispatcher deals blocks
+    // to the 8 XCDs round robin (block b -> XCD b % 8), each XCD with its own
+    // L2; give every XCD one contiguous range of work items so the blocks
+    // sharing a tile's activations (same m-tile) or an expert's weights (same
+    // expert, neighbouring m-tiles) run on one L2.
+    const int work = tiles[2 * max_tiles] * ntl;
+    const int chunk = (work + kXcds - 1) / kXcds;
+    const int xi = blockIdx.x / kXcds;
+    const int L = (blockIdx.x % kXcds) * chunk + xi;
+    if (xi >= chunk || L >= work) return;
+    const int mt = L / ntl, nt = L - mt * ntl;
+    const int row0 = tiles[2 * mt], info = tiles[2 * mt + 1];
+    const int e = info & 0xFFFF, nvalid = info >> 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int S = K / 64;
+    const size_t RB = (size_t)S * kChunk;               // bytes per activation term row
+
+    // Rows past the tile's pairs repeat its last pair (their results are not stored).
+    if (tid < kGemmRows) {
+        const int i = row0 + (tid < nvalid ? tid : nvalid - 1);
+        s_src[tid] = kGateUp ? sorted[i] / k : i;
+    }
+
+    // This block's output fragments [fa, fb); this wave's [wf0, wf0 + wcnt).
+    const int nfrag = NOUT / 32;
+    const int fa = (int)((int64_t)nfrag * nt / ntl), fb = (int)((int64_t)nfrag * (nt + 1) / ntl);
+    const int wf0 = fa + wave * kWaveFrags;
+    const int wcnt = max(0, min(kWaveFrags, fb - wf0));
+    const int R = kGateUp ? 2 * F : NOUT;               // weight rows per expert
+    const int nblk = K / 32;
+    uint32_t aoff[NA];                                  // byte offset of this lane's A piece in wq
+    // The E8M0 scales of a 32-row weight fragment are one contiguous,
+    // 16-byte aligned run of 32 * nblk = K bytes; each wave copies its
+    // fragments' runs into its own LDS area once.
+    uint8_t* wave_sc = lds + 2 * kBufBytes + (size_t)wave * NA * K;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        const int slot = kGateUp ? (a & 1) : a;         // gate/up: a = 0, 1 gate; 2, 3 up
+        const int f = slot < wcnt ? wf0 + slot : fa;    // idle fragments recompute fragment fa
+        const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
+        aoff[a] = (uint32_t)(((size_t)e * R + frow + n) * (size_t)(K / 2) + 16 * g);
+    }
+    auto copy_weight_scales = [&]() {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            const int slot = kGateUp ? (a & 1) : a;
+            const int f = slot < wcnt ? wf0 + slot : fa;
+            const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
+            const uint8_t* run = wsc + ((size_t)e * R + frow) * nblk;
+            for (int i = lane; i < K / 16; i += 64)
+                *reinterpret_cast<u32x4_t*>(wave_sc + a * K + 16 * i) =
+                    *reinterpret_cast<const u32x4_t*>(run + 16 * i);
+        }
+    };
+    // this lane's scale bytes: row n of each fragment, block 2 s + g at + 2 s
+    const uint8_t* my_sc = wave_sc + n * nblk + g;
+    __syncthreads();
+
+    // Staging: piece p = tid + 256 c (p < 128 kRowPieces) is 16-byte piece
+    // p % kRowPieces of row p / kRowPieces's step chunk, copied to byte 16 p
+    // of the LDS slot.
+    uint32_t gsrc[kPieces];                             // byte offsets in bq (< 4 GiB)
+#pragma unroll
+    for (int c = 0; c < kPieces; ++c) {
+        const int p = min(tid + kGemmThreads * c, kGemmRows * kRowPieces - 1);
+        const int r = p / kRowPieces;
+        gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * (p - r * kRowPieces));
+    }
+    auto piece_live = [&](int c) { return kGemmThreads * c + tid < kGemmRows * kRowPieces; };
+
+    f32x16_t acc[NA][4];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][j][i] = 0.f;
+
+    // Stage i = steps kStage i .. kStage i + kStage - 1, in LDS buffer i % 2.
+    u32x4_t a_cur[kStage][NA], a_nxt[kStage][NA];
+    u32x4_t br[kStage][kPieces];
+    const int nst = S / kStage;                         // whole stages; a partial one may follow
+
+    auto load_stage = [&](int i) {                      // global -> registers (steps clamped)
+#pragma unroll
+        for (int kk = 0; kk < kStage; ++kk) {
+            const uint32_t s = (uint32_t)min(i * kStage + kk, S - 1);
+            const uint32_t so = s * kChunk;
+#pragma unroll
+            for (int c = 0; c < kPieces; ++c)
+                if (piece_live(c)) br[kk][c] = *reinterpret_cast<const u32x4_t*>(bq + (gsrc[c] + so));
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+                a_nxt[kk][a] = *reinterpret_cast<const u32x4_t*>(wq + (aoff[a] + 32u * s));
+        }
+    };
+    auto store_stage = [&](int buf) {                   // registers -> LDS buffer
+#pragma unroll
+        for (int kk = 0; kk < kStage; ++kk) {
+            uint8_t* base = lds + buf * kBufBytes + kk * kSlotBytes;
+#pragma unroll
+            for (int c = 0; c < kPieces; ++c)
+                if (piece_live(c))
+                    *reinterpret_cast<u32x4_t*>(base + 16 * (tid + kGemmThreads * c)) = br[kk][c];
+        }
+    };
+    auto advance_a = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < kStage; ++kk)
+#pragma unroll
+            for (int a = 0; a < NA; ++a) a_cur[kk][a] = a_nxt[kk][a];
+    };
+    // Products of one stage, software-pipelined over its 4 kStage fragment
+    // groups (step kk, pair fragment j): group q + 1's operands are read from
+    // LDS while group q's products run, so two groups' operands are live.
+    struct Frag {
+        u32x4_t lo[NT], hi[NT];
+        uint32_t sw0, sw1;
+    };
+    auto read_frag = [&](int buf, int kk, int j, Frag& fr) {
+        // this lane's row (pair 32 j + n) of the step: term t's bytes of lane
+        // group g at 64 t + 32 g, its term scales (byte 2 t + g) at NT * 64
+        const uint8_t* row = lds + buf * kBufBytes + kk * kSlotBytes + (32 * j + n) * kChunk;
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(row + NT * 64);
+        fr.sw0 = sp[0] >> (8 * g);
+        fr.sw1 = NT > 2 ? sp[1] >> (8 * g) : 0u;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            fr.lo[t] = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g);
+            fr.hi[t] = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g + 16);
+        }
+    };
+    auto mfma_frag = [&](int kk, int j, const Frag& fr, const int (&as)[NA]) {
+        static_for<NT>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            const i32x8_t b8 = {(int)fr.lo[t][0], (int)fr.lo[t][1], (int)fr.lo[t][2], (int)fr.lo[t][3],
+                                (int)fr.hi[t][0], (int)fr.hi[t][1], (int)fr.hi[t][2], (int)fr.hi[t][3]};
+            const int bs = (int)(t < 2 ? fr.sw0 : fr.sw1);
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                const i32x8_t a8 = {(int)a_cur[kk][a][0], (int)a_cur[kk][a][1],
+                                    (int)a_cur[kk][a][2], (int)a_cur[kk][a][3], 0, 0, 0, 0};
+                // cbsz = 4: A is fp4 (E2M1); blgp = 0: B is fp8 (E4M3);
+                // B scale = byte 2 (t % 2) of its (shifted) scale word
+                acc[a][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    a8, b8, acc[a][j], 4, 0, 0, as[a], 2 * (t & 1), bs);
+            }
+        });
+    };
+    // nsteps (<= kStage) steps of the stage in buffer buf, first step s0
+    auto compute_stage = [&](int buf, int s0, int nsteps) {
+        Frag fr[2];
+        int as[kStage][NA];
+#pragma unroll
+        for (int kk = 0; kk < kStage; ++kk)
+#pragma unroll
+            for (int a = 0; a < NA; ++a) as[kk][a] = my_sc[a * K + 2 * min(s0 + kk, S - 1)];
+        read_frag(buf, 0, 0, fr[0]);
+        static_for<4 * kStage>([&](auto qc) {
+            constexpr int q = decltype(qc)::value, kk = q / 4, j = q % 4;
+            if (kk < nsteps) {
+                if constexpr (q + 1 < 4 * kStage) {
+                    if ((q + 1) / 4 < nsteps) read_frag(buf, (q + 1) / 4, (q + 1) % 4, fr[(q + 1) & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_frag(kk, j, fr[q & 1], as[kk]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+
+    // prologue: stage 0 in LDS buffer 0 (its loads overlap the weight-scale
+    // copy), stage 1 in flight
+    load_stage(0);
+    copy_weight_scales();
+    store_stage(0);
+    advance_a();
+    load_stage(1);
+    __syncthreads();
+    // Stage i: products from buffer i % 2; then stage i + 1 (loaded during
+    // stage i - 1) to the other buffer, and stage i + 2's loads issued, so
+    // every load has a whole stage of products to hide behind.
+    for (int i = 0; i < nst; ++i) {
+        compute_stage(i & 1, i * kStage, kStage);
+        __builtin_amdgcn_sched_barrier(0);
+        store_stage((i & 1) ^ 1);
+        advance_a();
+        load_stage(i + 2);
+        __syncthreads();
+    }
+    if (nst * kStage < S) compute_stage(nst & 1, nst * kStage, S - nst * kStage);   // partial
+
+    if constexpr (kGateUp) {
+        // h = silu(g) * u for features 32 f .. 32 f + 31 (block f of the down
+        // contraction) -> 3 fp8 terms.  Lanes n and n + 32 hold the block's
+        // two halves for pair n.
+        constexpr int kChunkH = term_chunk(3);
+        const size_t RBh = (size_t)(F / 64) * kChunkH;
+#pragma unroll
+        for (int ff = 0; ff < kWaveFrags; ++ff) {
+            if (ff >= wcnt) break;
+            const int f = wf0 + ff, sF = f >> 1, hb = f & 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 32 * j + n;
+                const bool live = r < nvalid;
+                float h[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) h[i] = silu_f32(acc[ff][j][i]) * acc[2 + ff][j][i];
+                uint8_t* ochunk = hq + (size_t)(row0 + r) * RBh + (size_t)sF * kChunkH;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    float amax = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    const int se = fp8_term_exponent(amax);
+                    const float inv = exp2i_neg(se), sc = exp2i(se);
+                    uint32_t q[4];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        q[w] = pack4_fp8(h[4 * w] * inv, h[4 * w + 1] * inv, h[4 * w + 2] * inv,
+                                         h[4 * w + 3] * inv);
+                    if (t < 2) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) sub4_fp8(h + 4 * w, q[w], sc);
+                    }
+                    if (live) {
+                        // elements 8 w + 4 g .. + 3 of the block
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            *reinterpret_cast<uint32_t*>(ochunk + t * 64 + (w >> 1) * 32 + 16 * hb +
+                                                         (w & 1) * 8 + 4 * g) = q[w];
+                        if (g == 0) ochunk[3 * 64 + 2 * t + hb] = (uint8_t)(se + 127);
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            if (a >= wcnt) break;
+            const int f = wf0 + a;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 32 * j + n;
+                if (r < nvalid) {
+                    float* orow = y + (size_t)(row0 + r) * NOUT + 32 * f + 4 * g;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        *reinterpret_cast<f32x4_t*>(orow + 8 * w) =
+                            f32x4_t{acc[a][j][4 * w], acc[a][j][4 * w + 1], acc[a][j][4 * w + 2],
+                                    acc[a][j][4 * w + 3]};
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int gemm_max_tiles(int T, int E, int k) {
+    const int64_t P = (int64_t)T * k;
+    const int64_t busy = P < E ? P : E;
+    return (int)((P + busy * (kGemmRows - 1) + kGemmRows - 1) / kGemmRows);
+}
+
+size_t gemm_term_bytes(int rows, int K, int NT) {
+    return (size_t)rows * (K / 64) * term_chunk(NT);
+}
+
+// Blocks for up to max_tiles x ntl work items, a multiple of the XCD count.
+static int64_t gemm_grid(int max_tiles, int ntl) {
+    const int64_t w = (int64_t)max_tiles * ntl;
+    return (w + kXcds - 1) / kXcds * kXcds;
+}
+
+// Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps
+// plus 4 waves x 4 fragments of weight scales (K bytes each).
+size_t gemm_lds_bytes(int K, int NT, int stage) {
+    return (size_t)2 * stage * kGemmRows * term_chunk(NT) + (size_t)16 * K;
+}
+
+// Steps per stage.  Two-step stages (fewer barriers) need more registers
+// than the 256 VGPRs left beside the accumulators; one step for now.
+static int gemm_stage(int, int) { return 1; }
+
+template <bool kGateUp, int kStage>
+static hipError_t launch_gemm(const MlpPlan& p, int ntl, const uint8_t* bq, const int32_t* sorted,
+                              const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
+                              int K, int NOUT, uint8_t* hq, float* y, hipStream_t stream) {
+    const size_t lds = gemm_lds_bytes(K, kGateUp ? 2 : 3, kStage);
+    if (lds > 65536) {
+        const hipError_t er = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (er != hipSuccess) return er;
+    }
+    hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, kStage>),
+                       dim3((unsigned)gemm_grid(p.max_tiles, ntl)), dim3(kGemmThreads), lds,
+                       stream, bq, sorted, p.k, wq, ws, tiles, p.max_tiles, ntl, K, NOUT, p.F,
+                       hq, y);
+    return hipSuccess;
+}
+
+static int gemm_col_tiles(int NOUT, int frags_per_block) {
+    return (NOUT / 32 + frags_per_block - 1) / frags_per_block;
+}
+
+hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+                           const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
+                           const int32_t* offsets, const int32_t* sorted, float* y, char* base,
+                           hipEvent_t* events, hipStream_t stream) {
+    uint8_t* xq = reinterpret_cast<uint8_t*>(base + p.off_xq);
+    uint8_t* hq = reinterpret_cast<uint8_t*>(base + p.off_hq);
+    int32_t* tiles = reinterpret_cast<int32_t*>(base + p.off_tiles);
+    hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(256), 0, stream, offsets, p.E,
+                       p.max_tiles, tiles);
+    const int64_t nsplit = (int64_t)p.T * (p.D / 64);
+    hipLaunchKernelGGL(split_terms_kernel<2>, dim3((unsigned)((nsplit + 255) / 256)), dim3(256), 0,
+                       stream, x, p.T, p.D, xq);
+    if (events) {
+        const hipError_t er = hipEventRecord(events[0], stream);
+        if (er != hipSuccess) return er;
+    }
+    hipError_t er;
+    const int ntl1 = gemm_col_tiles(p.F, 4 * 2);
+    er = gemm_stage(p.D, 2) == 2
+        ? launch_gemm<true, 2>(p, ntl1, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq, nullptr, stream)
+        : launch_gemm<true, 1>(p, ntl1, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq, nullptr, stream);
+    if (er != hipSuccess) return er;
+    if (events) {
+        er = hipEventRecord(events[1], stream);
+        if (er != hipSuccess) return er;
+    }
+    const int ntl2 = gemm_col_tiles(p.D, 4 * 4);
+    er = gemm_stage(p.F, 3) == 2
+        ? launch_gemm<false, 2>(p, ntl2, hq, nullptr, w2q, w2s, tiles, p.F, p.D, nullptr, y, stream)
+        : launch_gemm<false, 1>(p, ntl2, hq, nullptr, w2q, w2s, tiles, p.F, p.D, nullptr, y, stream);
+    if (er != hipSuccess) return er;
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -30,8 +30,6 @@ namespace moe {
 
 constexpr int kMaxSS = 6;    // super-steps of activations a wave keeps in registers
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
-
 // h[row, f] for the rows of expert e (sorted order), fp16.
 __global__ __launch_bounds__(256) void gateup_stream_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13q,
@@ -236,8 +234,6 @@ constexpr int kMaxWaveTiles = 4;       // tiles a wavefront owns (outputs held i
 //
 // LDS, per unit: data [nss][NT][64 lanes][32 B], then scales [nss][NT][64].
 
-typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
-
 __device__ __forceinline__ f32x4_t mfma_fp4w_fp8x(u32x4_t w, int wscale, const u32x4_t (&b)[2],
                                                  int bscale, f32x4_t c) {
     i32x8_t a8 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
@@ -305,26 +301,15 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
             float amax = 0.f;
 #pragma unroll
             for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(v[n]));
-            // s = floor(log2 amax) - 7 puts the block maximum in [128, 256) (E4M3 max 448)
-            int se = amax > 0.f ? (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF) - 127 - 7 : 0;
-            se = se < -127 ? -127 : se;
-            const float inv = __builtin_bit_cast(float, (uint32_t)(127 - se) << 23);   // 2^-s, s >= -120
-            const float sc = se >= -126 ? __builtin_bit_cast(float, (uint32_t)(127 + se) << 23)
-                                        : __builtin_bit_cast(float, 0x00400000u);    // 2^s
+            const int se = fp8_term_exponent(amax);
+            const float inv = exp2i_neg(se), sc = exp2i(se);
             uint32_t q[8];
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w] * inv, v[4 * w + 1] * inv, 0, false);
-                pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2] * inv, v[4 * w + 3] * inv, pk, true);
-                q[w] = (uint32_t)pk;
-            }
+            for (int w = 0; w < 8; ++w)
+                q[w] = pack4_fp8(v[4 * w] * inv, v[4 * w + 1] * inv, v[4 * w + 2] * inv,
+                                 v[4 * w + 3] * inv);
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                v[4 * w] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 0) * sc;
-                v[4 * w + 1] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 1) * sc;
-                v[4 * w + 2] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 2) * sc;
-                v[4 * w + 3] -= __builtin_amdgcn_cvt_f32_fp8((int)q[w], 3) * sc;
-            }
+            for (int w = 0; w < 8; ++w) sub4_fp8(v + 4 * w, q[w], sc);
             uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -606,9 +591,28 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     MlpPlan p{};
     p.T = T; p.D = D; p.F = F; p.E = E; p.k = k;
     const size_t P = (size_t)T * k;
-    p.off_h = 0;
-    p.off_y = align256(P * F * sizeof(_Float16));
-    p.ws_bytes = align256(p.off_y + P * D * sizeof(float));
+    // (the grouped GEMM addresses its buffers with 32-bit byte offsets)
+    const size_t k4G = (size_t)1 << 32;
+    p.gemm_ok = D % 64 == 0 && F % 64 == 0 && gemm_lds_bytes(D, 2, 1) <= kGemmMaxLds &&
+                gemm_lds_bytes(F, 3, 1) <= kGemmMaxLds && gemm_term_bytes(T, D, 2) < k4G &&
+                gemm_term_bytes((int)P, F, 3) < k4G && (size_t)E * F * D < k4G;
+    // Weight streaming reads every touched expert's weights once per 16 of its
+    // pairs; the grouped GEMM stages 128-pair tiles.  Switch once the average
+    // expert receives 32 pairs.
+    p.gemm_auto = p.gemm_ok && P >= (size_t)32 * E;
+    p.max_tiles = gemm_max_tiles(T, E, k);
+    p.off_y = 0;
+    const size_t scratch = align256(P * D * sizeof(float));
+    p.off_h = scratch;
+    const size_t stream_end = align256(p.off_h + P * F * sizeof(_Float16));
+    size_t gemm_end = scratch;
+    if (p.gemm_ok) {
+        p.off_xq = scratch;
+        p.off_hq = align256(p.off_xq + gemm_term_bytes(T, D, 2));
+        p.off_tiles = align256(p.off_hq + gemm_term_bytes((int)P, F, 3));
+        gemm_end = align256(p.off_tiles + sizeof(int32_t) * (2 * (size_t)p.max_tiles + 1));
+    }
+    p.ws_bytes = std::max(stream_end, gemm_end);
     return p;
 }
 
@@ -639,7 +643,11 @@ static int blocks_per_expert(int E, int ntiles) {
     return bpe < 1 ? 1 : bpe;
 }
 
-hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
+                                 const int32_t* pos, uint16_t* out, hipEvent_t* events,
+                                 hipStream_t stream);
+
+hipError_t launch_mlp(const MlpPlan& p, int algo, const uint16_t* x, const uint8_t* w13q,
                       const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                       const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                       const int32_t* pos, uint16_t* out, void* ws, hipEvent_t* events,
@@ -647,6 +655,13 @@ hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
     char* base = static_cast<char*>(ws);
     _Float16* h = reinterpret_cast<_Float16*>(base + p.off_h);
     float* y = reinterpret_cast<float*>(base + p.off_y);
+    const bool gemm = algo == 2 || (algo == 0 && p.gemm_auto);
+    if (gemm) {
+        const hipError_t er = launch_mlp_gemm(p, x, w13q, w13s, w2q, w2s, offsets, sorted, y,
+                                              base, events, stream);
+        if (er != hipSuccess) return er;
+        return launch_combine(p, y, topk_w, pos, out, events, stream);
+    }
     if (events) {
         const hipError_t er = hipEventRecord(events[0], stream);
         if (er != hipSuccess) return er;
@@ -689,6 +704,12 @@ hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
         hipLaunchKernelGGL(down_stream_kernel, dim3(p.E * bpe2), dim3(256), 0, stream, h, w2q,
                            w2s, offsets, p.D, p.F, bpe2, y);
     }
+    return launch_combine(p, y, topk_w, pos, out, events, stream);
+}
+
+static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
+                                 const int32_t* pos, uint16_t* out, hipEvent_t* events,
+                                 hipStream_t stream) {
     if (events) {
         const hipError_t er = hipEventRecord(events[2], stream);
         if (er != hipSuccess) return er;

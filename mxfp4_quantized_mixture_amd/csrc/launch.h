@@ -25,15 +25,34 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
                         int32_t* sorted, int32_t* pos, float* logits_out, void* ws,
                         hipStream_t stream);
 
+// Workspace of moe_expert_mlp: y (fp32 [P, D], both paths) followed by the
+// scratch of whichever path runs (the two share one region).
 struct MlpPlan {
     int T, D, F, E, k;
-    size_t off_h, off_y, ws_bytes;
+    bool gemm_ok;        // grouped-GEMM path possible: D % 64 == 0 and F % 64 == 0
+    bool gemm_auto;      // grouped-GEMM path chosen when the caller leaves it open
+    int max_tiles;       // upper bound of 128-pair tiles over all experts
+    size_t off_y;
+    size_t off_h;                                    // streaming: h fp16 [P, F]
+    size_t off_xq, off_hq, off_tiles;              // grouped GEMM
+    size_t ws_bytes;
 };
 MlpPlan plan_mlp(int T, int D, int F, int E, int k);
-hipError_t launch_mlp(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+// algo: 0 = automatic, 1 = weight streaming, 2 = grouped GEMM (requires gemm_ok)
+hipError_t launch_mlp(const MlpPlan& p, int algo, const uint16_t* x, const uint8_t* w13q,
                       const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                       const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                       const int32_t* pos, uint16_t* out, void* ws, hipEvent_t* events,
                       hipStream_t stream);
+
+// grouped-GEMM path (expert_gemm.hip)
+int gemm_max_tiles(int T, int E, int k);
+size_t gemm_term_bytes(int rows, int K, int NT);
+size_t gemm_lds_bytes(int K, int NT, int stage);
+constexpr size_t kGemmMaxLds = 159 * 1024;    // of 160 KiB; the rest is static LDS
+hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+                           const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
+                           const int32_t* offsets, const int32_t* sorted, float* y, char* base,
+                           hipEvent_t* events, hipStream_t stream);
 
 }  // namespace moe

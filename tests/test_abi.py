@@ -115,6 +115,30 @@ def test_mlp_validation(L):
     assert _mlp(L, w13=FAKE + 4) == ALIGN
 
 
+def _mlp_ex(L, algo, T=8, D=64, F=64, E=4, k=2, out=FAKE):
+    ws_bytes = L.moe_expert_mlp_workspace_size(T, D, F, E, k) or 1 << 20
+    return L.moe_expert_mlp_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, D, F,
+                               E, k, out, FAKE, ws_bytes, algo, None, None)
+
+
+def test_mlp_algorithm_validation(L):
+    assert _mlp_ex(L, 3) == ENUM
+    assert _mlp_ex(L, -1) == ENUM
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, D=96) == SHAPE      # grouped GEMM needs D % 64
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=160) == SHAPE     # ... and F % 64
+    assert _mlp_ex(L, moe.MLP_STREAM, out=None) == NULL
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, out=None) == NULL
+
+
+def test_mlp_workspace_covers_both_algorithms(L):
+    T, D, F, E, k = 8192, 2880, 2880, 32, 4
+    P = T * k
+    n = L.moe_expert_mlp_workspace_size(T, D, F, E, k)
+    y = 4 * P * D
+    assert n >= y + 2 * P * F                      # streaming: y + fp16 h
+    assert n >= y + 2 * T * D + 3 * P * F          # grouped GEMM: y + x and h fp8 terms
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

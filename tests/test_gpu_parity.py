@@ -198,12 +198,12 @@ class Inputs:
         self.w13, self.w2 = MI.gen_experts(cfg, seed, threads=G.THREADS)
 
 
-def run_gpu_layer(inp):
+def run_gpu_layer(inp, algo=moe.MLP_AUTO):
     cfg = inp.cfg
     xd = G.bf16_dev(inp.x)
     weights = moe.ExpertWeights.quantize(G.bf16_dev(inp.w13), G.bf16_dev(inp.w2))
     r = moe.moe_route(xd, G.f32_dev(inp.wr), G.f32_dev(inp.b), cfg.k)
-    out = moe.moe_expert_mlp(xd, weights, r)
+    out = moe.moe_expert_mlp(xd, weights, r, algo=algo)
     torch.cuda.synchronize()
     return weights, r, out
 
@@ -221,9 +221,9 @@ def sample_tokens(ids, T, rng, n_random=12):
     return np.array(sorted(toks))
 
 
-def check_layer(inp, tokens="all", what=""):
+def check_layer(inp, tokens="all", what="", algo=moe.MLP_AUTO):
     cfg = inp.cfg
-    weights, r, out = run_gpu_layer(inp)
+    weights, r, out = run_gpu_layer(inp, algo)
     ref_r = O.route(inp.x, inp.wr, inp.b, cfg.k)
     ok_tok = np.nonzero(ref_r["gap"] >= NEAR_TIE)[0]
     gids = r.ids.cpu().numpy()
@@ -283,6 +283,46 @@ EDGE = [
 @pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
 def test_layer_edge_shapes(cfg):
     check_layer(Inputs(cfg, 3), what=cfg.name)
+
+
+# Shapes for the grouped-GEMM path (128-pair tiles, 32-wide output fragments,
+# 64-element contraction steps in groups of 3): ragged last tiles, tiles
+# whose fragments leave wavefronts idle, step counts that are not multiples
+# of 3, experts with a single pair, one expert with many tiles, E = 256.
+GEMM_EDGE = [
+    MI.MoEConfig("gemm_ragged", T=300, D=192, F=320, E=5, k=2),
+    MI.MoEConfig("gemm_one_expert_many_tiles", T=1000, D=128, F=128, E=1, k=1),
+    MI.MoEConfig("gemm_sparse_experts", T=40, D=64, F=64, E=64, k=2),
+    MI.MoEConfig("gemm_skewed", T=2000, D=256, F=192, E=16, k=4, bias="zipf"),
+    MI.MoEConfig("gemm_full_width", T=512, D=2880, F=2880, E=8, k=2),
+    MI.MoEConfig("gemm_wide_router", T=700, D=128, F=64, E=256, k=8),
+    MI.MoEConfig("gemm_outliers", T=256, D=512, F=256, E=4, k=2, outliers=True),
+    MI.MoEConfig("gemm_long_contraction", T=300, D=4096, F=4160, E=2, k=1),
+]
+
+
+@pytest.mark.parametrize("cfg", GEMM_EDGE, ids=[c.name for c in GEMM_EDGE])
+def test_layer_grouped_gemm_shapes(cfg):
+    check_layer(Inputs(cfg, 4), what=cfg.name + "/grouped-gemm", algo=moe.MLP_GROUPED_GEMM)
+
+
+@pytest.mark.parametrize("name", ["gemm_skewed", "gemm_full_width"])
+def test_layer_streaming_on_gemm_shapes(name):
+    cfg = {c.name: c for c in GEMM_EDGE}[name]
+    check_layer(Inputs(cfg, 4), what=name + "/stream", algo=moe.MLP_STREAM)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gptoss20b_decode"])
+def test_layer_grouped_gemm_on_decode_shapes(name):
+    check_layer(Inputs(MI.CONFIGS[name], 2), what=name + "/grouped-gemm",
+                algo=moe.MLP_GROUPED_GEMM)
+
+
+def test_grouped_gemm_is_deterministic():
+    inp = Inputs(GEMM_EDGE[3], 1)
+    _, _, a = run_gpu_layer(inp, moe.MLP_GROUPED_GEMM)
+    _, _, b = run_gpu_layer(inp, moe.MLP_GROUPED_GEMM)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_layer_is_deterministic():
