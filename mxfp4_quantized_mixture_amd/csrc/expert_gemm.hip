@@ -28,6 +28,7 @@
 // t of block 2s + h (the rest of the last 16 bytes is padding).  Codes and
 // scales of a step travel together, so staging a step is one contiguous copy
 // per row.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -37,10 +38,33 @@
 namespace moe {
 
 constexpr int kGemmRows = 128;      // routed pairs per tile: 4 fragments of 32
-constexpr int kGemmThreads = 256;   // 4 wavefronts, one per SIMD
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
+// Wavefront layouts (row groups x pair groups), measured on the 20B-shaped
+// prefill: gate/up 2 x 2 (two blocks per CU), down 4 x 2 (one block of 8).
+constexpr int kScaleIters = 8;      // weight-scale copy: K <= 64 lanes x 16 bytes x 8
+static_assert(64 * 16 * kScaleIters == kGemmMaxContraction, "scale copy covers every K");
 
 __host__ __device__ constexpr int term_chunk(int NT) { return NT * 64 + 16; }
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's 16 bytes at
+// base + voff land at LDS byte lds_base + 16 l (lds_base wave-uniform).
+// Issued as an opaque instruction so the compiler does not order later LDS
+// reads behind it (it cannot tell that they read other buffers); callers
+// wait for it with wait_vm_all() before the barrier that publishes the data.
+// It writes no registers (m0, which holds the LDS destination, is restored),
+// and an untracked memory operation can only make the compiler's own
+// memory-counter waits stricter.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, const uint8_t* lds_dst) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(m0v), "v"(voff), "s"(base));
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt not waited for)
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
 template <int N, typename Fn, int... I>
@@ -136,8 +160,10 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM.  Block = one tile of kGemmRows pairs x one column range of
-// output fragments (32 outputs each).  Four wavefronts, each owning all 128
-// pairs (4 B fragments) and kWaveFrags output fragments:
+// output fragments (32 outputs each).  Four wavefronts in WR row groups x
+// 4 / WR pair groups; each owns 128 / (4 / WR) pairs (NB B fragments) and
+// kWaveFrags output fragments (WR = 4: one block per CU with 128 x 128
+// accumulator tiles; WR = 2: two blocks per CU with 128 x 64 tiles):
 //   gate/up: 2 feature fragments -> 4 A fragments (their gate and up rows),
 //            epilogue h = silu(g) * u written as 3-term rows;
 //   down:    4 output fragments -> 4 A fragments, epilogue y (fp32).
@@ -146,14 +172,16 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 // buffers, weights global -> registers, each a stage ahead, with one
 // barrier per stage.
 // ---------------------------------------------------------------------------
-template <bool kGateUp, int kStage>
-__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
+template <bool kGateUp, int kStage, int WR, int WP>
+__global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kernel(
     const uint8_t* __restrict__ bq, const int32_t* __restrict__ sorted, int k,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
     uint8_t* __restrict__ hq, float* __restrict__ y) {
     constexpr int NT = kGateUp ? 2 : 3;                 // activation terms
     constexpr int NA = 4;                               // A fragments per wave
+    constexpr int kGemmThreads = 64 * WR * WP;
+    constexpr int NB = 4 / WP;                          // B fragments (32 pairs) per wave
     constexpr int kWaveFrags = kGateUp ? 2 : 4;         // output fragments per wave
     constexpr int kChunk = term_chunk(NT);
     // LDS slot of one step: the 128 rows' step chunks, row-major.  The row
@@ -181,6 +209,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
     const int row0 = tiles[2 * mt], info = tiles[2 * mt + 1];
     const int e = info & 0xFFFF, nvalid = info >> 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WP, wp = wave % WP;           // this wave's row group and pair group
     const int n = lane & 31, g = lane >> 5;
     const int S = K / 64;
     const size_t RB = (size_t)S * kChunk;               // bytes per activation term row
@@ -193,8 +222,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
 
     // This block's output fragments [fa, fb); this wave's [wf0, wf0 + wcnt).
     const int nfrag = NOUT / 32;
-    const int fa = (int)((int64_t)nfrag * nt / ntl), fb = (int)((int64_t)nfrag * (nt + 1) / ntl);
-    const int wf0 = fa + wave * kWaveFrags;
+    // (gate/up: whole 64-feature steps per block, so each wave's two feature
+    // fragments form one step of the h term rows; down: an even split)
+    const int fa = kGateUp ? nt * 2 * WR : (int)((int64_t)nfrag * nt / ntl);
+    const int fb = kGateUp ? min(fa + 2 * WR, nfrag) : (int)((int64_t)nfrag * (nt + 1) / ntl);
+    const int wf0 = fa + wr * kWaveFrags;
     const int wcnt = max(0, min(kWaveFrags, fb - wf0));
     const int R = kGateUp ? 2 * F : NOUT;               // weight rows per expert
     const int nblk = K / 32;
@@ -202,7 +234,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
     // The E8M0 scales of a 32-row weight fragment are one contiguous,
     // 16-byte aligned run of 32 * nblk = K bytes; each wave copies its
     // fragments' runs into its own LDS area once.
-    uint8_t* wave_sc = lds + 2 * kBufBytes + (size_t)wave * NA * K;
+    // (the WP wavefronts of a row group share one copy, made by wp == 0)
+    uint8_t* wave_sc = lds + 2 * kBufBytes + (size_t)wr * NA * K;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
         const int slot = kGateUp ? (a & 1) : a;         // gate/up: a = 0, 1 gate; 2, 3 up
@@ -210,25 +243,34 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
         const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
         aoff[a] = (uint32_t)(((size_t)e * R + frow + n) * (size_t)(K / 2) + 16 * g);
     }
+    // Direct global -> LDS loads (lane l writes 16 bytes at the wave-uniform
+    // destination + 16 l), all issued before the prologue barrier, so the
+    // copy is one memory round trip and holds no registers.
     auto copy_weight_scales = [&]() {
+        if (wp != 0) return;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             const int slot = kGateUp ? (a & 1) : a;
             const int f = slot < wcnt ? wf0 + slot : fa;
             const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
             const uint8_t* run = wsc + ((size_t)e * R + frow) * nblk;
-            for (int i = lane; i < K / 16; i += 64)
-                *reinterpret_cast<u32x4_t*>(wave_sc + a * K + 16 * i) =
-                    *reinterpret_cast<const u32x4_t*>(run + 16 * i);
+#pragma unroll
+            for (int it = 0; it < kScaleIters; ++it) {
+                const int i = lane + 64 * it;
+                if (64 * it < K / 16 && i < K / 16)
+                    dma16(wsc, (uint32_t)((size_t)(run - wsc) + 16 * i), wave_sc + a * K + 16 * 64 * it);
+            }
         }
     };
     // this lane's scale bytes: row n of each fragment, block 2 s + g at + 2 s
     const uint8_t* my_sc = wave_sc + n * nblk + g;
+    uint8_t* dummy = lds + 2 * kBufBytes + (size_t)WR * NA * K + (wave & 7) * 1024;
     __syncthreads();
 
     // Staging: piece p = tid + 256 c (p < 128 kRowPieces) is 16-byte piece
-    // p % kRowPieces of row p / kRowPieces's step chunk, copied to byte 16 p
-    // of the LDS slot.
+    // p % kRowPieces of row p / kRowPieces's step chunk, loaded straight into
+    // byte 16 p of the LDS slot (direct global -> LDS loads: a wave's 64
+    // pieces land contiguously at a wave-uniform destination).
     uint32_t gsrc[kPieces];                             // byte offsets in bq (< 4 GiB)
 #pragma unroll
     for (int c = 0; c < kPieces; ++c) {
@@ -236,42 +278,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
         const int r = p / kRowPieces;
         gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * (p - r * kRowPieces));
     }
-    auto piece_live = [&](int c) { return kGemmThreads * c + tid < kGemmRows * kRowPieces; };
 
-    f32x16_t acc[NA][4];
+    f32x16_t acc[NA][NB];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][j][i] = 0.f;
 
     // Stage i = steps kStage i .. kStage i + kStage - 1, in LDS buffer i % 2.
     u32x4_t a_cur[kStage][NA], a_nxt[kStage][NA];
-    u32x4_t br[kStage][kPieces];
     const int nst = S / kStage;                         // whole stages; a partial one may follow
 
-    auto load_stage = [&](int i) {                      // global -> registers (steps clamped)
+    // stage i: activation steps -> LDS buffer i % 2, weights -> a_nxt (steps clamped)
+    auto load_stage = [&](int i) {
 #pragma unroll
         for (int kk = 0; kk < kStage; ++kk) {
-            const uint32_t s = (uint32_t)min(i * kStage + kk, S - 1);
-            const uint32_t so = s * kChunk;
+            const uint32_t st = (uint32_t)min(i * kStage + kk, S - 1);
+            const uint32_t so = st * kChunk;
+            uint8_t* slot = lds + (i & 1) * kBufBytes + kk * kSlotBytes;
+            // (a wave whose pieces lie past the slot, in the last round, loads
+            // a duplicate into its dummy area: no branches in the loop)
 #pragma unroll
-            for (int c = 0; c < kPieces; ++c)
-                if (piece_live(c)) br[kk][c] = *reinterpret_cast<const u32x4_t*>(bq + (gsrc[c] + so));
+            for (int c = 0; c < kPieces; ++c) {
+                const bool real = kGemmThreads * c + wave * 64 < kGemmRows * kRowPieces;
+                dma16(bq, gsrc[c] + so, real ? slot + 16 * (kGemmThreads * c + wave * 64) : dummy);
+            }
 #pragma unroll
             for (int a = 0; a < NA; ++a)
-                a_nxt[kk][a] = *reinterpret_cast<const u32x4_t*>(wq + (aoff[a] + 32u * s));
-        }
-    };
-    auto store_stage = [&](int buf) {                   // registers -> LDS buffer
-#pragma unroll
-        for (int kk = 0; kk < kStage; ++kk) {
-            uint8_t* base = lds + buf * kBufBytes + kk * kSlotBytes;
-#pragma unroll
-            for (int c = 0; c < kPieces; ++c)
-                if (piece_live(c))
-                    *reinterpret_cast<u32x4_t*>(base + 16 * (tid + kGemmThreads * c)) = br[kk][c];
+                a_nxt[kk][a] = *reinterpret_cast<const u32x4_t*>(wq + (aoff[a] + 32u * st));
         }
     };
     auto advance_a = [&]() {
@@ -280,130 +316,146 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
 #pragma unroll
             for (int a = 0; a < NA; ++a) a_cur[kk][a] = a_nxt[kk][a];
     };
-    // Products of one stage, software-pipelined over its 4 kStage fragment
-    // groups (step kk, pair fragment j): group q + 1's operands are read from
-    // LDS while group q's products run, so two groups' operands are live.
+    // Products of one stage, software-pipelined over its kStage x NB x NT
+    // operand groups (step kk, pair fragment j, term t): group q + 1's B
+    // operand is read from LDS while group q's NA products run, so two
+    // groups' operands (8 registers each) are live.
     struct Frag {
-        u32x4_t lo[NT], hi[NT];
-        uint32_t sw0, sw1;
+        u32x4_t lo, hi;
+        uint32_t sw;                                    // scale word, byte 2 (t % 2) selected
     };
-    auto read_frag = [&](int buf, int kk, int j, Frag& fr) {
+    auto read_frag = [&](int buf, int kk, int j, int t, Frag& fr) {
         // this lane's row (pair 32 j + n) of the step: term t's bytes of lane
         // group g at 64 t + 32 g, its term scales (byte 2 t + g) at NT * 64
-        const uint8_t* row = lds + buf * kBufBytes + kk * kSlotBytes + (32 * j + n) * kChunk;
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(row + NT * 64);
-        fr.sw0 = sp[0] >> (8 * g);
-        fr.sw1 = NT > 2 ? sp[1] >> (8 * g) : 0u;
+        const uint8_t* row = lds + buf * kBufBytes + kk * kSlotBytes + (32 * (wp * NB + j) + n) * kChunk;
+        fr.sw = reinterpret_cast<const uint32_t*>(row + NT * 64)[t >> 1] >> (8 * g);
+        fr.lo = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g);
+        fr.hi = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g + 16);
+    };
+    auto mfma_frag = [&](int kk, int j, auto tc, const Frag& fr, const int (&as)[NA]) {
+        constexpr int t = decltype(tc)::value;
+        const i32x8_t b8 = {(int)fr.lo[0], (int)fr.lo[1], (int)fr.lo[2], (int)fr.lo[3],
+                            (int)fr.hi[0], (int)fr.hi[1], (int)fr.hi[2], (int)fr.hi[3]};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            fr.lo[t] = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g);
-            fr.hi[t] = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g + 16);
+        for (int a = 0; a < NA; ++a) {
+            const i32x8_t a8 = {(int)a_cur[kk][a][0], (int)a_cur[kk][a][1],
+                                (int)a_cur[kk][a][2], (int)a_cur[kk][a][3], 0, 0, 0, 0};
+            // cbsz = 4: A is fp4 (E2M1); blgp = 0: B is fp8 (E4M3);
+            // B scale = byte 2 (t % 2) of its (shifted) scale word
+            acc[a][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a8, b8, acc[a][j], 4, 0, 0, as[a], 2 * (t & 1), (int)fr.sw);
         }
     };
-    auto mfma_frag = [&](int kk, int j, const Frag& fr, const int (&as)[NA]) {
-        static_for<NT>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            const i32x8_t b8 = {(int)fr.lo[t][0], (int)fr.lo[t][1], (int)fr.lo[t][2], (int)fr.lo[t][3],
-                                (int)fr.hi[t][0], (int)fr.hi[t][1], (int)fr.hi[t][2], (int)fr.hi[t][3]};
-            const int bs = (int)(t < 2 ? fr.sw0 : fr.sw1);
-#pragma unroll
-            for (int a = 0; a < NA; ++a) {
-                const i32x8_t a8 = {(int)a_cur[kk][a][0], (int)a_cur[kk][a][1],
-                                    (int)a_cur[kk][a][2], (int)a_cur[kk][a][3], 0, 0, 0, 0};
-                // cbsz = 4: A is fp4 (E2M1); blgp = 0: B is fp8 (E4M3);
-                // B scale = byte 2 (t % 2) of its (shifted) scale word
-                acc[a][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a8, b8, acc[a][j], 4, 0, 0, as[a], 2 * (t & 1), bs);
-            }
-        });
-    };
-    // nsteps (<= kStage) steps of the stage in buffer buf, first step s0
-    auto compute_stage = [&](int buf, int s0, int nsteps) {
+    // nsteps (<= kStage) steps of the stage in buffer buf, first step s0;
+    // after_first() runs once the first group's products are issued
+    auto compute_stage = [&](int buf, int s0, int nsteps, auto&& after_first) {
+        constexpr int kGroups = kStage * NB * NT;
         Frag fr[2];
         int as[kStage][NA];
 #pragma unroll
         for (int kk = 0; kk < kStage; ++kk)
 #pragma unroll
             for (int a = 0; a < NA; ++a) as[kk][a] = my_sc[a * K + 2 * min(s0 + kk, S - 1)];
-        read_frag(buf, 0, 0, fr[0]);
-        static_for<4 * kStage>([&](auto qc) {
-            constexpr int q = decltype(qc)::value, kk = q / 4, j = q % 4;
+        read_frag(buf, 0, 0, 0, fr[0]);
+        static_for<kGroups>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int kk = q / (NB * NT), j = (q / NT) % NB, t = q % NT;
             if (kk < nsteps) {
-                if constexpr (q + 1 < 4 * kStage) {
-                    if ((q + 1) / 4 < nsteps) read_frag(buf, (q + 1) / 4, (q + 1) % 4, fr[(q + 1) & 1]);
+                if constexpr (q + 1 < kGroups) {
+                    constexpr int q1 = q + 1;
+                    if (q1 / (NB * NT) < nsteps)
+                        read_frag(buf, q1 / (NB * NT), (q1 / NT) % NB, q1 % NT, fr[q1 & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_frag(kk, j, fr[q & 1], as[kk]);
+                mfma_frag(kk, j, std::integral_constant<int, t>{}, fr[q & 1], as[kk]);
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (q == 0) {
+                    after_first();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         });
     };
 
-    // prologue: stage 0 in LDS buffer 0 (its loads overlap the weight-scale
-    // copy), stage 1 in flight
-    load_stage(0);
+    // prologue: weight scales and stage 0 in LDS (one round trip; the
+    // barrier's release waits for the direct loads)
     copy_weight_scales();
-    store_stage(0);
-    advance_a();
-    load_stage(1);
+    load_stage(0);
+    wait_vm_all();
     __syncthreads();
-    // Stage i: products from buffer i % 2; then stage i + 1 (loaded during
-    // stage i - 1) to the other buffer, and stage i + 2's loads issued, so
-    // every load has a whole stage of products to hide behind.
+    advance_a();
+    // Stage i: products from buffer i % 2, with stage i + 1's loads issued
+    // right after the first group of them (its buffer was last read in stage
+    // i - 1); the barrier at the end waits for the loads, so each has almost
+    // a whole stage to land.
     for (int i = 0; i < nst; ++i) {
-        compute_stage(i & 1, i * kStage, kStage);
-        __builtin_amdgcn_sched_barrier(0);
-        store_stage((i & 1) ^ 1);
-        advance_a();
-        load_stage(i + 2);
+        compute_stage(i & 1, i * kStage, kStage, [&]() { load_stage(i + 1); });
+        wait_vm_all();
         __syncthreads();
+        advance_a();
     }
-    if (nst * kStage < S) compute_stage(nst & 1, nst * kStage, S - nst * kStage);   // partial
+    if (nst * kStage < S)                               // partial last stage
+        compute_stage(nst & 1, nst * kStage, S - nst * kStage, []() {});
 
     if constexpr (kGateUp) {
         // h = silu(g) * u for features 32 f .. 32 f + 31 (block f of the down
         // contraction) -> 3 fp8 terms.  Lanes n and n + 32 hold the block's
-        // two halves for pair n.
+        // two halves for pair n.  A wave's two fragments are one 64-feature
+        // step; it assembles its pairs' step chunks in LDS (free now), then
+        // writes them with contiguous 16-byte stores.
         constexpr int kChunkH = term_chunk(3);
+        constexpr int kWavePairs = 32 * NB;
         const size_t RBh = (size_t)(F / 64) * kChunkH;
+        __syncthreads();                                // every wave is done with the stage buffers
+        uint8_t* wst = lds + wave * (kWavePairs * kChunkH);
+        if (wcnt > 0) {
+            const int sF = wf0 >> 1;
 #pragma unroll
-        for (int ff = 0; ff < kWaveFrags; ++ff) {
-            if (ff >= wcnt) break;
-            const int f = wf0 + ff, sF = f >> 1, hb = f & 1;
+            for (int ff = 0; ff < 2; ++ff) {
+                const int hb = ff;                      // fragment wf0 + ff, wf0 even
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 32 * j + n;
-                const bool live = r < nvalid;
-                float h[16];
+                for (int j = 0; j < NB; ++j) {
+                    float h[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) h[i] = silu_f32(acc[ff][j][i]) * acc[2 + ff][j][i];
-                uint8_t* ochunk = hq + (size_t)(row0 + r) * RBh + (size_t)sF * kChunkH;
+                    for (int i = 0; i < 16; ++i) h[i] = silu_f32(acc[ff][j][i]) * acc[2 + ff][j][i];
+                    uint8_t* chunk = wst + (32 * j + n) * kChunkH;
 #pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    float amax = 0.f;
+                    for (int t = 0; t < 3; ++t) {
+                        float amax = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
-                    amax = fmaxf(amax, __shfl_xor(amax, 32));
-                    const int se = fp8_term_exponent(amax);
-                    const float inv = exp2i_neg(se), sc = exp2i(se);
-                    uint32_t q[4];
+                        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
+                        amax = fmaxf(amax, __shfl_xor(amax, 32));
+                        const int se = fp8_term_exponent(amax);
+                        const float inv = exp2i_neg(se), sc = exp2i(se);
+                        uint32_t q[4];
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        q[w] = pack4_fp8(h[4 * w] * inv, h[4 * w + 1] * inv, h[4 * w + 2] * inv,
-                                         h[4 * w + 3] * inv);
-                    if (t < 2) {
+                        for (int w = 0; w < 4; ++w)
+                            q[w] = pack4_fp8(h[4 * w] * inv, h[4 * w + 1] * inv, h[4 * w + 2] * inv,
+                                             h[4 * w + 3] * inv);
+                        if (t < 2) {
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) sub4_fp8(h + 4 * w, q[w], sc);
-                    }
-                    if (live) {
+                            for (int w = 0; w < 4; ++w) sub4_fp8(h + 4 * w, q[w], sc);
+                        }
                         // elements 8 w + 4 g .. + 3 of the block
 #pragma unroll
                         for (int w = 0; w < 4; ++w)
-                            *reinterpret_cast<uint32_t*>(ochunk + t * 64 + (w >> 1) * 32 + 16 * hb +
+                            *reinterpret_cast<uint32_t*>(chunk + t * 64 + (w >> 1) * 32 + 16 * hb +
                                                          (w & 1) * 8 + 4 * g) = q[w];
-                        if (g == 0) ochunk[3 * 64 + 2 * t + hb] = (uint8_t)(se + 127);
+                        if (g == 0) chunk[3 * 64 + 2 * t + hb] = (uint8_t)(se + 127);
                     }
                 }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // pairs wp * kWavePairs .. + kWavePairs - 1 of the tile, step sF
+            const int pr0 = wp * kWavePairs;
+            for (int pc = lane; pc < kWavePairs * (kChunkH / 16); pc += 64) {
+                const int pr = pc / (kChunkH / 16), piece = pc - pr * (kChunkH / 16);
+                if (pr0 + pr < nvalid)
+                    *reinterpret_cast<u32x4_t*>(hq + (size_t)(row0 + pr0 + pr) * RBh +
+                                                (size_t)sF * kChunkH + 16 * piece) =
+                        *reinterpret_cast<const u32x4_t*>(wst + pr * kChunkH + 16 * piece);
             }
         }
     } else {
@@ -412,8 +464,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_kernel(
             if (a >= wcnt) break;
             const int f = wf0 + a;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 32 * j + n;
+            for (int j = 0; j < NB; ++j) {
+                const int r = 32 * (wp * NB + j) + n;
                 if (r < nvalid) {
                     float* orow = y + (size_t)(row0 + r) * NOUT + 32 * f + 4 * g;
 #pragma unroll
@@ -447,37 +499,38 @@ static int64_t gemm_grid(int max_tiles, int ntl) {
     return (w + kXcds - 1) / kXcds * kXcds;
 }
 
-// Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps
-// plus 4 waves x 4 fragments of weight scales (K bytes each).
-size_t gemm_lds_bytes(int K, int NT, int stage) {
-    return (size_t)2 * stage * kGemmRows * term_chunk(NT) + (size_t)16 * K;
+static int gemm_col_tiles(int NOUT, int frags_per_block) {
+    return (NOUT / 32 + frags_per_block - 1) / frags_per_block;
 }
 
-// Steps per stage.  Two-step stages (fewer barriers) need more registers
-// than the 256 VGPRs left beside the accumulators; one step for now.
-static int gemm_stage(int, int) { return 1; }
+// Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps
+// plus 4 waves x 4 fragments of weight scales (K bytes each).
+size_t gemm_lds_bytes(int K, int NT, int stage, int wr) {
+    return (size_t)2 * stage * kGemmRows * term_chunk(NT) + (size_t)4 * wr * K + 8 * 1024;
+}
 
-template <bool kGateUp, int kStage>
-static hipError_t launch_gemm(const MlpPlan& p, int ntl, const uint8_t* bq, const int32_t* sorted,
+
+template <bool kGateUp, int kStage, int WR, int WP>
+static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t* sorted,
                               const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
                               int K, int NOUT, uint8_t* hq, float* y, hipStream_t stream) {
-    const size_t lds = gemm_lds_bytes(K, kGateUp ? 2 : 3, kStage);
+    const int ntl = gemm_col_tiles(NOUT, WR * (kGateUp ? 2 : 4));
+    size_t lds = gemm_lds_bytes(K, kGateUp ? 2 : 3, kStage, WR);
+    if (kGateUp)                                        // epilogue staging of the h term rows
+        lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * term_chunk(3));
     if (lds > 65536) {
         const hipError_t er = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage>),
+            reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage, WR, WP>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (er != hipSuccess) return er;
     }
-    hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, kStage>),
-                       dim3((unsigned)gemm_grid(p.max_tiles, ntl)), dim3(kGemmThreads), lds,
+    hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, kStage, WR, WP>),
+                       dim3((unsigned)gemm_grid(p.max_tiles, ntl)), dim3(64 * WR * WP), lds,
                        stream, bq, sorted, p.k, wq, ws, tiles, p.max_tiles, ntl, K, NOUT, p.F,
                        hq, y);
     return hipSuccess;
 }
 
-static int gemm_col_tiles(int NOUT, int frags_per_block) {
-    return (NOUT / 32 + frags_per_block - 1) / frags_per_block;
-}
 
 hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
@@ -496,19 +549,13 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w
         if (er != hipSuccess) return er;
     }
     hipError_t er;
-    const int ntl1 = gemm_col_tiles(p.F, 4 * 2);
-    er = gemm_stage(p.D, 2) == 2
-        ? launch_gemm<true, 2>(p, ntl1, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq, nullptr, stream)
-        : launch_gemm<true, 1>(p, ntl1, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq, nullptr, stream);
+    er = launch_gemm<true, 1, 2, 2>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq, nullptr, stream);
     if (er != hipSuccess) return er;
     if (events) {
         er = hipEventRecord(events[1], stream);
         if (er != hipSuccess) return er;
     }
-    const int ntl2 = gemm_col_tiles(p.D, 4 * 4);
-    er = gemm_stage(p.F, 3) == 2
-        ? launch_gemm<false, 2>(p, ntl2, hq, nullptr, w2q, w2s, tiles, p.F, p.D, nullptr, y, stream)
-        : launch_gemm<false, 1>(p, ntl2, hq, nullptr, w2q, w2s, tiles, p.F, p.D, nullptr, y, stream);
+    er = launch_gemm<false, 1, 4, 2>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D, nullptr, y, stream);
     if (er != hipSuccess) return er;
     return hipGetLastError();
 }

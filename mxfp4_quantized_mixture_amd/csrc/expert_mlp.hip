@@ -593,8 +593,9 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     const size_t P = (size_t)T * k;
     // (the grouped GEMM addresses its buffers with 32-bit byte offsets)
     const size_t k4G = (size_t)1 << 32;
-    p.gemm_ok = D % 64 == 0 && F % 64 == 0 && gemm_lds_bytes(D, 2, 1) <= kGemmMaxLds &&
-                gemm_lds_bytes(F, 3, 1) <= kGemmMaxLds && gemm_term_bytes(T, D, 2) < k4G &&
+    p.gemm_ok = D % 64 == 0 && F % 64 == 0 && D <= kGemmMaxContraction &&
+                F <= kGemmMaxContraction && gemm_lds_bytes(D, 2, 1, 4) <= kGemmMaxLds &&
+                gemm_lds_bytes(F, 3, 1, 4) <= kGemmMaxLds && gemm_term_bytes(T, D, 2) < k4G &&
                 gemm_term_bytes((int)P, F, 3) < k4G && (size_t)E * F * D < k4G;
     // Weight streaming reads every touched expert's weights once per 16 of its
     // pairs; the grouped GEMM stages 128-pair tiles.  Switch once the average

@@ -48,8 +48,9 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, const uint16_t* x, const uint8
 // grouped-GEMM path (expert_gemm.hip)
 int gemm_max_tiles(int T, int E, int k);
 size_t gemm_term_bytes(int rows, int K, int NT);
-size_t gemm_lds_bytes(int K, int NT, int stage);
+size_t gemm_lds_bytes(int K, int NT, int stage, int wr);
 constexpr size_t kGemmMaxLds = 159 * 1024;    // of 160 KiB; the rest is static LDS
+constexpr int kGemmMaxContraction = 8192;      // D and F limit of the grouped GEMM
 hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                            const int32_t* offsets, const int32_t* sorted, float* y, char* base,
