@@ -13,6 +13,8 @@
 //   route_topk_kernel      one wavefront per token: k rounds of wave-wide
 //                          DPP argmax, softmax over the k, per-chunk histogram
 //   route_finish_kernel    few pairs: histogram, scan and scatter in one block
+//   route_small_kernel     few tokens (T <= 64): top-k, softmax, histogram,
+//                          scan and scatter together in one block
 //   route_scan_kernel      many pairs: per-expert running sums over chunks
 //   route_scatter_kernel   many pairs: stable scatter, ranks from ballots
 // Nothing uses floating-point atomics, so results are deterministic.
@@ -358,6 +360,78 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(
     scatter_chunk(pair_e, P, 0, base_e, E, seg_base, sorted, pos);
 }
 
+// Few tokens (T <= kSmallTokens, T E <= kSmallLogits): one block of 16
+// wavefronts sums the router slices of every (token, expert) logit into LDS
+// (each thread's slice loads all in flight at once), then does the top-k and
+// softmax of every token (token t on wavefront t % 16), the histogram, the
+// scan and the stable scatter of the T k pairs -- one launch instead of
+// route_topk_kernel + route_finish_kernel.
+constexpr int kSmallTokens = 64;
+constexpr int kSmallLogits = 8192;
+
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ P, int S, int T, int E, int k, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
+    __shared__ float lg[kSmallLogits];
+    __shared__ int cnt[kMaxE];
+    __shared__ int pair_e[kSmallTokens * kMaxK];
+    __shared__ int seg_base[8 * kMaxE];
+    __shared__ int base_e[kMaxE];
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kMaxE; i += blockDim.x) cnt[i] = 0;
+    constexpr int kMaxS = 16;
+    const int n = T * E;
+    for (int i = tid; i < n; i += blockDim.x) {
+        float part[kMaxS];
+#pragma unroll
+        for (int sp = 0; sp < kMaxS; ++sp) part[sp] = sp < S ? P[(int64_t)sp * n + i] : 0.f;
+        float acc = part[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxS; ++sp)
+            if (sp < S) acc += part[sp];
+        lg[i] = acc;
+        if (logits_out) logits_out[i] = acc;
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += 16) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + 64 * q;
+            v[q] = e < E ? lg[t * E + e] : 0.f;
+        }
+        float my_v;
+        int my_i;
+        wave_topk(v[0], v[1], v[2], v[3], E, k, my_v, my_i);
+        const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+        const float ex = lane < k ? expf(my_v - top) : 0.f;
+        float den = 0.f;
+        for (int j = 0; j < k; ++j)
+            den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+        if (lane < k) {
+            ids[(int64_t)t * k + lane] = my_i;
+            wts[(int64_t)t * k + lane] = ex / den;
+            pair_e[t * k + lane] = my_i;
+        }
+    }
+    __syncthreads();
+    const int npairs = T * k;
+    for (int p = tid; p < npairs; p += blockDim.x) atomicAdd(&cnt[pair_e[p]], 1);
+    __syncthreads();
+    const int c = tid < E ? cnt[tid] : 0;
+    const int excl = block_exclusive_scan(c, wsum);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = excl;
+        base_e[tid] = excl;
+        if (tid == E - 1) offsets[E] = excl + c;
+    }
+    __syncthreads();
+    scatter_chunk(pair_e, npairs, 0, base_e, E, seg_base, sorted, pos);
+}
+
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const int32_t* __restrict__ chunk_counts, int32_t* __restrict__ chunk_base, int chunks,
     int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
@@ -437,6 +511,11 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
         dim3 g((p.E + 15) / 16, (p.T + 63) / 64, p.splits);
         hipLaunchKernelGGL(router_logits_kernel<4>, g, dim3(kRouterWaves * 64), 0, stream, x, wr,
                            br, P, p.T, p.D, p.E, p.splits);
+    }
+    if (p.T <= kSmallTokens && p.T * p.E <= kSmallLogits) {
+        hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, stream, P, p.splits, p.T,
+                           p.E, p.k, logits_out, ids, w, counts, offsets, sorted, pos);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL(route_topk_kernel, dim3(p.chunks), dim3(kChunkTokens * 64), 0, stream, P,
                        p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts);
