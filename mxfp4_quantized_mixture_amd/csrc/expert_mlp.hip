@@ -213,7 +213,6 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kStreamWaves = 8;
-constexpr int kNB = 4;                 // super-steps per load batch
 constexpr int kMaxWaveTiles = 4;       // tiles a wavefront owns (outputs held in registers)
 
 // Staged activations.  The weights enter the matrix cores exactly as stored
@@ -322,22 +321,22 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
     }
 }
 
-template <int NS>
+template <int NB>
 struct WBatch {
-    u32x4_t q[NS][kNB];
+    u32x4_t q[NB];
 };
 
-// Load kNB super-steps (from ss0) of NS weight rows; out-of-range blocks are
-// clamped to the row's last block (finite data, multiplied by zero activations).
-template <int NS>
-__device__ __forceinline__ void load_batch(WBatch<NS>& B, const uint8_t* const (&q)[NS], int ss0,
-                                           int g, int nblk) {
+// Load NB super-steps (from ss0) of one 16-row weight tile (this lane's row
+// q); out-of-range blocks are clamped to the row's last block (finite data,
+// multiplied by zero activations).
+template <int NB>
+__device__ __forceinline__ void load_batch(WBatch<NB>& B, const uint8_t* q, int ss0, int g,
+                                           int nblk) {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) {
+    for (int i = 0; i < NB; ++i) {
         int blk = (ss0 + i) * 4 + g;
         blk = blk < nblk ? blk : nblk - 1;
-#pragma unroll
-        for (int r = 0; r < NS; ++r) B.q[r][i] = *reinterpret_cast<const u32x4_t*>(q[r] + blk * 16);
+        B.q[i] = *reinterpret_cast<const u32x4_t*>(q + blk * 16);
     }
 }
 
@@ -380,20 +379,20 @@ __device__ __forceinline__ void commit_scales(const ScaleRegs<NS>& S, uint8_t* b
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NS, int NT>
-__device__ __forceinline__ void compute_batch(const WBatch<NS>& B, int ss0, int nss,
+// acc += this batch's NB super-steps of the tile times the staged terms;
+// wsc is this lane's row of the tile's committed scale run.
+template <int NB, int NT>
+__device__ __forceinline__ void compute_batch(const WBatch<NB>& B, int ss0, int nss,
                                               const uint8_t* lds, const uint8_t* lds_scales,
                                               const uint8_t* wsc, int lane, int g, int nblk,
-                                              f32x4_t (&acc)[NS]) {
+                                              f32x4_t& acc) {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) {
+    for (int i = 0; i < NB; ++i) {
         const int ss = ss0 + i;
         if (ss < nss) {
             int blk = ss * 4 + g;
             blk = blk < nblk ? blk : nblk - 1;
-            int wscale[NS];
-#pragma unroll
-            for (int r = 0; r < NS; ++r) wscale[r] = wsc[r * 16 * nblk + blk];
+            const int wscale = wsc[blk];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint8_t* frag = lds + ((size_t)(ss * NT + t) * 64 + lane) * 32;
@@ -401,9 +400,7 @@ __device__ __forceinline__ void compute_batch(const WBatch<NS>& B, int ss0, int 
                 bx[0] = *reinterpret_cast<const u32x4_t*>(frag);
                 bx[1] = *reinterpret_cast<const u32x4_t*>(frag + 16);
                 const int bs = lds_scales[(ss * NT + t) * 64 + lane];
-#pragma unroll
-                for (int r = 0; r < NS; ++r)
-                    acc[r] = mfma_fp4w_fp8x(B.q[r][i], wscale[r], bx, bs, acc[r]);
+                acc = mfma_fp4w_fp8x(B.q[i], wscale, bx, bs, acc);
             }
         }
     }
@@ -412,6 +409,11 @@ __device__ __forceinline__ void compute_batch(const WBatch<NS>& B, int ss0, int 
 // kGateUp: A = [gate rows; up rows] of W13 (NS = 2), B = x rows (2 fp8 terms),
 //          epilogue h = silu(g) * u -> fp16.
 // else:    A = W2 rows (NS = 1), B = h rows (3 fp8 terms), epilogue y -> fp32.
+//
+// A wavefront streams one weight row range at a time: for each of its tiles
+// the gate rows over the whole contraction, then the up rows (the gate sums
+// wait in registers).  Two concurrent row streams per wavefront, 4 MB apart,
+// sustain measurably less HBM bandwidth than one.
 //
 // Block b streams a fixed range of 16-row tiles of expert b / bpe, so its
 // first weight and scale loads are issued at entry, before the routing is
@@ -424,8 +426,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted, int D, int F, int E, int k, int bpe,
     void* __restrict__ out) {
-    constexpr int NS = kGateUp ? 2 : 1;
+    constexpr int NS = kGateUp ? 2 : 1;      // row streams per tile, taken in turn
     constexpr int NT = kGateUp ? 2 : 3;
+    constexpr int NB = kGateUp ? 8 : 4;      // super-steps per load batch
+    // ring depth: two batches of 8 for gate/up, three of 4 for down
+    constexpr int kRing = kGateUp ? 2 : 3;
     extern __shared__ __align__(16) uint8_t lds_stage[];
     __shared__ int s_row[16];
     const int K = kGateUp ? D : F;           // contraction length
@@ -436,23 +441,21 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int nblk = K / 32, nss = (nblk + 3) / 4, nbt = (nss + kNB - 1) / kNB;
+    const int nblk = K / 32, nss = (nblk + 3) / 4, nbt = (nss + NB - 1) / NB;
+    const int seg = NS * nbt;                // steps (load batches) per tile
     const size_t rowbytes = (size_t)K / 2;
     const uint8_t* lds_scales = lds_stage + (size_t)nss * NT * 64 * 32;
     uint8_t* wave_sc = lds_stage + (size_t)nss * NT * 64 * 33 + (size_t)wave * NS * 16 * nblk;
     const uint8_t* wsc = wave_sc + m * nblk;        // this lane's row of the committed run
     const int my_tiles = a + wave < b ? (b - a - wave + kStreamWaves - 1) / kStreamWaves : 0;
-    const int steps = my_tiles * nbt;
+    const int steps = my_tiles * seg;
     const uint8_t* qe = wq + (size_t)e * (kGateUp ? 2 * F : D) * rowbytes;
     const uint8_t* se = ws + (size_t)e * (kGateUp ? 2 * F : D) * nblk;
 
-    auto rows_of = [&](int s, const uint8_t* (&q)[NS]) {
-        const int tile = a + wave + (s / nbt) * kStreamWaves;
-#pragma unroll
-        for (int r = 0; r < NS; ++r) {
-            const int row = r * F + tile * 16 + m;     // up rows follow the F gate rows
-            q[r] = qe + (size_t)row * rowbytes;
-        }
+    auto row_of = [&](int s) {
+        const int tile = a + wave + (s / seg) * kStreamWaves;
+        const int r = NS == 1 ? 0 : (s / nbt) % NS;   // up rows follow the F gate rows
+        return qe + (size_t)(r * F + tile * 16 + m) * rowbytes;
     };
     auto runs_of = [&](int tile, const uint8_t* (&run)[NS]) {
 #pragma unroll
@@ -463,16 +466,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     // compiler never has to drain the load queue at a branch; only the
     // compute is predicated.
     const int last = steps > 0 ? steps - 1 : 0;
-    auto fetch = [&](WBatch<NS>& W, int s) {
+    auto fetch = [&](WBatch<NB>& W, int s) {
         const int sc_ = s < last ? s : last;
-        const uint8_t* q[NS];
-        rows_of(sc_, q);
-        load_batch<NS>(W, q, (sc_ % nbt) * kNB, g, nblk);
+        load_batch<NB>(W, row_of(sc_), (sc_ % nbt) * NB, g, nblk);
     };
-    // ring depth: three batches for down (one weight stream), two for gate/up
-    // (two streams; a third would not fit the register file)
-    constexpr int kRing = kGateUp ? 2 : 3;
-    WBatch<NS> B0, B1, B2;
+    WBatch<NB> B0, B1, B2;
     ScaleRegs<NS> SR;
     auto prologue = [&]() {
         if (steps > 0) {
@@ -498,9 +496,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
         stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row);
         __syncthreads();
 
-        f32x4_t acc[NS];
-#pragma unroll
-        for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc_gate = {0.f, 0.f, 0.f, 0.f};
         // Tile results stay in registers until the wave has issued its last
         // load: on gfx9 the vector memory counter also covers stores, so an
         // early store would make later load waits wait for its write too.
@@ -508,31 +504,37 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
         typedef typename std::conditional<kGateUp, f16x4_t, f32x4_t>::type OutT;
         OutT obuf[kMaxWaveTiles];
         auto epilogue = [&](int s) {
-            const int j = s / nbt;
+            const int j = s / seg;
             OutT res;
             if constexpr (kGateUp) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) res[q] = (_Float16)(silu_f32(acc[0][q]) * acc[1][q]);
+                for (int q = 0; q < 4; ++q) res[q] = (_Float16)(silu_f32(acc_gate[q]) * acc[q]);
             } else {
-                res = acc[0];
+                res = acc;
             }
 #pragma unroll
             for (int jj = 0; jj < kMaxWaveTiles; ++jj)
                 if (jj == j) obuf[jj] = res;
-#pragma unroll
-            for (int r = 0; r < NS; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         };
-        auto consume = [&](const WBatch<NS>& W, int s) {
-            if (s % nbt == 0) {               // tile switch: commit its scales, fetch the next's
+        auto consume = [&](const WBatch<NB>& W, int s) {
+            if (s % seg == 0) {               // tile switch: commit its scales, fetch the next's
                 commit_scales<NS>(SR, wave_sc, lane, nblk);
-                const int nxt = s + nbt < steps ? s + nbt : s;
+                const int nxt = s + seg < steps ? s + seg : s;
                 const uint8_t* run[NS];
-                runs_of(a + wave + (nxt / nbt) * kStreamWaves, run);
+                runs_of(a + wave + (nxt / seg) * kStreamWaves, run);
                 fetch_scales<NS>(SR, run, lane, nblk);
             }
-            compute_batch<NS, NT>(W, (s % nbt) * kNB, nss, lds_stage, lds_scales, wsc, lane, g,
-                                  nblk, acc);
-            if (s % nbt == nbt - 1) epilogue(s);
+            const int r = NS == 1 ? 0 : (s / nbt) % NS;
+            compute_batch<NB, NT>(W, (s % nbt) * NB, nss, lds_stage, lds_scales,
+                                  wsc + r * 16 * nblk, lane, g, nblk, acc);
+            if (s % nbt == nbt - 1) {         // end of a row range
+                if (kGateUp && r == 0) {
+                    acc_gate = acc;           // gate sums wait for the up rows
+                } else {
+                    epilogue(s);
+                }
+                acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
         };
         for (int s = 0; s < steps; s += kRing) {
             consume(B0, s);
