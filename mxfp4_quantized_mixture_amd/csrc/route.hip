@@ -15,8 +15,9 @@
 //   route_finish_kernel    few pairs: histogram, scan and scatter in one block
 //   route_small_kernel     few tokens (T <= 64): top-k, softmax, histogram,
 //                          scan and scatter together in one block
-//   route_scan_kernel      many pairs: per-expert running sums over chunks
-//   route_scatter_kernel   many pairs: stable scatter, ranks from ballots
+//   route_scan_kernel      many pairs: per-expert scan of the chunk counts
+//   route_scatter_kernel   many pairs: expert offsets, stable scatter (ranks
+//                          from ballots)
 // Nothing uses floating-point atomics, so results are deterministic.
 #include <float.h>
 
@@ -432,39 +433,54 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     scatter_chunk(pair_e, npairs, 0, base_e, E, seg_base, sorted, pos);
 }
 
+// Many pairs, step 1: block e scans expert e's chunk counts.  Each thread
+// sums a contiguous run of chunks (its loads all in flight), the block scans
+// the run sums, and each thread writes its chunks' bases relative to the
+// expert's first pair; counts[e] is the total.
 __global__ __launch_bounds__(256) void route_scan_kernel(
     const int32_t* __restrict__ chunk_counts, int32_t* __restrict__ chunk_base, int chunks,
-    int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+    int E, int32_t* __restrict__ counts) {
     __shared__ int wsum[16];
-    const int e = threadIdx.x;
+    const int e = blockIdx.x;
+    const int per = (chunks + blockDim.x - 1) / blockDim.x;
+    const int c0 = threadIdx.x * per;
+    const int c1 = c0 + per < chunks ? c0 + per : chunks;
     int run = 0;
-    if (e < E) {
-        for (int c = 0; c < chunks; ++c) {
-            const int v = chunk_counts[(int64_t)c * E + e];
-            chunk_base[(int64_t)c * E + e] = run;
-            run += v;
-        }
+    for (int c = c0; c < c1; ++c) run += chunk_counts[(int64_t)c * E + e];
+    int base = block_exclusive_scan(run, wsum);
+    for (int c = c0; c < c1; ++c) {
+        const int v = chunk_counts[(int64_t)c * E + e];
+        chunk_base[(int64_t)c * E + e] = base;
+        base += v;
     }
-    const int excl = block_exclusive_scan(e < E ? run : 0, wsum);
-    if (e < E) {
-        counts[e] = run;
-        offsets[e] = excl;
-        if (e == E - 1) offsets[E] = excl + run;
-        for (int c = 0; c < chunks; ++c) chunk_base[(int64_t)c * E + e] += excl;
-    }
+    if (threadIdx.x == blockDim.x - 1) counts[e] = base;
 }
 
+// Many pairs, step 2: one block per chunk.  The expert offsets (an exclusive
+// scan of counts, E <= 256 = blockDim) are recomputed by every block, and
+// block 0 writes them out; the chunk's pairs are then scattered stably.
 __global__ __launch_bounds__(256) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ chunk_base, int T, int E,
-    int k, int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ counts, int T, int E, int k, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
     __shared__ int chunk_ids[kChunkTokens * kMaxK];
     __shared__ int seg_base[8 * kMaxE];
     __shared__ int base_e[kMaxE];
+    __shared__ int wsum[16];
     const int tbeg = blockIdx.x * kChunkTokens;
     const int ntok = T - tbeg < kChunkTokens ? T - tbeg : kChunkTokens;
     const int npairs = ntok * k;
     for (int i = threadIdx.x; i < npairs; i += blockDim.x) chunk_ids[i] = ids[(int64_t)tbeg * k + i];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) base_e[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+    const int e = threadIdx.x;
+    const int c = e < E ? counts[e] : 0;
+    const int excl = block_exclusive_scan(c, wsum);
+    if (e < E) {
+        base_e[e] = excl + chunk_base[(int64_t)blockIdx.x * E + e];
+        if (blockIdx.x == 0) {
+            offsets[e] = excl;
+            if (e == E - 1) offsets[E] = excl + c;
+        }
+    }
     __syncthreads();
     scatter_chunk(chunk_ids, npairs, tbeg * k, base_e, E, seg_base, sorted, pos);
 }
@@ -524,10 +540,10 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
         hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, p.E,
                            counts, offsets, sorted, pos);
     } else {
-        hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, stream, chunk_counts,
-                           chunk_base, p.chunks, p.E, counts, offsets);
+        hipLaunchKernelGGL(route_scan_kernel, dim3(p.E), dim3(256), 0, stream, chunk_counts,
+                           chunk_base, p.chunks, p.E, counts);
         hipLaunchKernelGGL(route_scatter_kernel, dim3(p.chunks), dim3(256), 0, stream, ids,
-                           chunk_base, p.T, p.E, p.k, sorted, pos);
+                           chunk_base, counts, p.T, p.E, p.k, offsets, sorted, pos);
     }
     return hipGetLastError();
 }
