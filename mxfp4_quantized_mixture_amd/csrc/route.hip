@@ -362,19 +362,75 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(
 }
 
 // Few tokens (T <= kSmallTokens, T E <= kSmallLogits): one block of 16
-// wavefronts sums the router slices of every (token, expert) logit into LDS
-// (each thread's slice loads all in flight at once), then does the top-k and
-// softmax of every token (token t on wavefront t % 16), the histogram, the
-// scan and the stable scatter of the T k pairs -- one launch instead of
-// route_topk_kernel + route_finish_kernel.
+// wavefronts does the whole routing in one launch.
+//  1. Sum the router slices of every (token, expert) logit into LDS (each
+//     thread has the slice loads of four logits in flight at once); rows are
+//     padded to E + 1 floats so that lanes reading one expert of different
+//     tokens hit different banks.
+//  2. Top-k with one lane per token: wavefront w keeps the best (logit, id)
+//     of its slice of experts in registers (insertion into a sorted list of
+//     k rounded up to a power of two; larger logit first, then lower id), and
+//     the 16 lists are merged pairwise through LDS (16 -> 8 -> 4 -> 2 -> 1).
+//     The order of the selections is the same total order as repeated
+//     argmax.
+//  3. Softmax over the k, histogram, scan and stable scatter.
 constexpr int kSmallTokens = 64;
 constexpr int kSmallLogits = 8192;
 
+// Insert (v, e) into the sorted K-list (bv, bi).
+template <int K>
+__device__ __forceinline__ void topk_insert(float (&bv)[K], int (&bi)[K], float v, int e) {
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        const bool b = ranks_before(v, e, bv[s], bi[s]);
+        const float tv = b ? bv[s] : v;
+        const int ti = b ? bi[s] : e;
+        bv[s] = b ? v : bv[s];
+        bi[s] = b ? e : bi[s];
+        v = tv;
+        e = ti;
+    }
+}
+
+// (av, ai) = the best K of two lists sorted best first (K a power of two):
+// picking the better of a[s] and b[K-1-s] leaves the best K as a bitonic
+// sequence, which log2 K compare-exchange stages sort.
+template <int K>
+__device__ __forceinline__ void topk_merge(float (&av)[K], int (&ai)[K], const float (&bv)[K],
+                                           const int (&bi)[K]) {
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        const bool b = ranks_before(bv[K - 1 - s], bi[K - 1 - s], av[s], ai[s]);
+        av[s] = b ? bv[K - 1 - s] : av[s];
+        ai[s] = b ? bi[K - 1 - s] : ai[s];
+    }
+#pragma unroll
+    for (int st = K / 2; st >= 1; st >>= 1) {
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            if ((s & st) == 0) {
+                const int u = s + st;
+                const bool b = ranks_before(av[u], ai[u], av[s], ai[s]);
+                const float tv = av[s];
+                const int ti = ai[s];
+                av[s] = b ? av[u] : av[s];
+                ai[s] = b ? ai[u] : ai[s];
+                av[u] = b ? tv : av[u];
+                ai[u] = b ? ti : ai[u];
+            }
+        }
+    }
+}
+
+template <int K>
 __global__ __launch_bounds__(1024) void route_small_kernel(
-    const float* __restrict__ P, int S, int T, int E, int k, float* __restrict__ logits_out,
+    const float* __restrict__ P, int S, int T, int E, float* __restrict__ logits_out,
     int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
-    __shared__ float lg[kSmallLogits];
+    constexpr int k = K;
+    constexpr int KP = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : 8;   // list length, a power of two
+    // logits [T][E + 1], later the merge lists: values [8][KP][64], ids after them
+    __shared__ float lg[kSmallLogits + kSmallTokens];
     __shared__ int cnt[kMaxE];
     __shared__ int pair_e[kSmallTokens * kMaxK];
     __shared__ int seg_base[8 * kMaxE];
@@ -392,29 +448,64 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 #pragma unroll
         for (int sp = 1; sp < kMaxS; ++sp)
             if (sp < S) acc += part[sp];
-        lg[i] = acc;
+        lg[i + i / E] = acc;                      // row t starts at t (E + 1)
         if (logits_out) logits_out[i] = acc;
     }
     __syncthreads();
-    for (int t = wave; t < T; t += 16) {
-        float v[4];
+
+    // 2. top-k, lane = token
+    float bv[KP];
+    int bi[KP];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = lane + 64 * q;
-            v[q] = e < E ? lg[t * E + e] : 0.f;
+    for (int s = 0; s < KP; ++s) {
+        bv[s] = -__builtin_inff();
+        bi[s] = 0x7FFFFFFF;                       // ranks after every real (logit, id)
+    }
+    const int t = lane;
+    {
+        const int eg = (E + 15) / 16;
+        const int e0 = wave * eg, e1 = min(E, e0 + eg);
+        if (t < T)
+            for (int e = e0; e < e1; ++e) topk_insert<KP>(bv, bi, lg[t * (E + 1) + e], e);
+    }
+    float* lv = lg;                               // [8][KP][64]
+    int* li = reinterpret_cast<int*>(lg + 8 * KP * 64);
+    for (int half = 8; half >= 1; half >>= 1) {
+        __syncthreads();                          // logits / previous lists no longer read
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int s = 0; s < KP; ++s) {
+                lv[((wave - half) * KP + s) * 64 + lane] = bv[s];
+                li[((wave - half) * KP + s) * 64 + lane] = bi[s];
+            }
         }
-        float my_v;
-        int my_i;
-        wave_topk(v[0], v[1], v[2], v[3], E, k, my_v, my_i);
-        const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
-        const float ex = lane < k ? expf(my_v - top) : 0.f;
+        __syncthreads();
+        if (wave < half && t < T) {
+            float ov[KP];
+            int oi[KP];
+#pragma unroll
+            for (int s = 0; s < KP; ++s) {
+                ov[s] = lv[(wave * KP + s) * 64 + lane];
+                oi[s] = li[(wave * KP + s) * 64 + lane];
+            }
+            topk_merge<KP>(bv, bi, ov, oi);
+        }
+    }
+    // 3. softmax over the k selected logits (bv[0] is the largest)
+    if (wave == 0 && t < T) {
+        float ex[K];
         float den = 0.f;
-        for (int j = 0; j < k; ++j)
-            den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
-        if (lane < k) {
-            ids[(int64_t)t * k + lane] = my_i;
-            wts[(int64_t)t * k + lane] = ex / den;
-            pair_e[t * k + lane] = my_i;
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            ex[s] = expf(bv[s] - bv[0]);
+            den += ex[s];
+        }
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            const int e = bi[s] < E ? bi[s] : E - 1;       // only with non-finite logits
+            ids[(int64_t)t * k + s] = e;
+            wts[(int64_t)t * k + s] = ex[s] / den;
+            pair_e[t * k + s] = e;
         }
     }
     __syncthreads();
@@ -529,8 +620,17 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
                            br, P, p.T, p.D, p.E, p.splits);
     }
     if (p.T <= kSmallTokens && p.T * p.E <= kSmallLogits) {
-        hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, stream, P, p.splits, p.T,
-                           p.E, p.k, logits_out, ids, w, counts, offsets, sorted, pos);
+        switch (p.k) {
+#define MOE_ROUTE_SMALL(K)                                                                    \
+    case K:                                                                                   \
+        hipLaunchKernelGGL(route_small_kernel<K>, dim3(1), dim3(1024), 0, stream, P, p.splits, \
+                           p.T, p.E, logits_out, ids, w, counts, offsets, sorted, pos);        \
+        break;
+            MOE_ROUTE_SMALL(1) MOE_ROUTE_SMALL(2) MOE_ROUTE_SMALL(3) MOE_ROUTE_SMALL(4)
+            MOE_ROUTE_SMALL(5) MOE_ROUTE_SMALL(6) MOE_ROUTE_SMALL(7) MOE_ROUTE_SMALL(8)
+#undef MOE_ROUTE_SMALL
+            default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     hipLaunchKernelGGL(route_topk_kernel, dim3(p.chunks), dim3(kChunkTokens * 64), 0, stream, P,
