@@ -251,50 +251,42 @@ __device__ __forceinline__ float act_to_f32(uint16_t v, bool is_bf16) {
 // gathered bf16 x rows for gate/up, contiguous fp16 h rows for down) as NT
 // fp8 terms.  One thread per (row, 32-element block); rows past nvalid and
 // blocks past K are zero with scale 2^0.
-template <int NT, bool kGather>
+//
+// after_loads() runs once every thread has issued the loads of its first
+// (row, block): the caller issues its weight prefetch there.  Loads complete
+// in issue order as far as the wait counter is concerned, so activation
+// loads issued behind a chip-wide weight prefetch would wait for all of it.
+template <int NT, bool kGather, typename F>
 __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __restrict__ sorted,
-                            int row0, int nvalid, int k, int K, uint8_t* lds, int* s_row) {
+                            int row0, int nvalid, int k, int K, uint8_t* lds, int* s_row,
+                            F&& after_loads) {
     if (threadIdx.x < 16)
         s_row[threadIdx.x] = threadIdx.x < nvalid
             ? (kGather ? sorted[row0 + threadIdx.x] / k : row0 + threadIdx.x) : -1;
+    __syncthreads();
     const int nblk = K / 32, nss = (nblk + 3) / 4;
     uint8_t* scales = lds + (size_t)nss * NT * 64 * 32;
-    // padding: rows past nvalid (all their blocks) and blocks past K -> zeros, scale 2^0
-    for (int task = threadIdx.x; task < 16 * nss * 4; task += blockDim.x) {
-        const int m = task & 15, blk = task >> 4;
-        if (m < nvalid && blk < nblk) continue;
-        const int ss = blk >> 2, gq = blk & 3;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
+    const int ntask = nvalid * nblk;
+    auto load_task = [&](int task, u32x4_t (&raw)[4]) {
+        const int m = task % nvalid, blk = task / nvalid;
+        const uint16_t* p = src + (int64_t)s_row[m] * K + blk * 32;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-                *reinterpret_cast<u32x4_t*>(base + (16 * (2 * (gq & 1) + half) + m) * 32 +
-                                            16 * (gq >> 1)) = z;
-            scales[(ss * NT + t) * 64 + gq * 16 + m] = 127;
-        }
-    }
-    __syncthreads();
-    // live (row, block) pairs only
-    for (int task = threadIdx.x; task < nvalid * nblk; task += blockDim.x) {
+        for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4_t*>(p + c * 8);
+    };
+    // Hardware K of element n of block gq is 32 gq + n: lanes 16 * (2 (gq & 1) + n / 16)
+    // + m, byte 16 (gq >> 1) + n % 16.
+    auto convert_task = [&](int task, const u32x4_t (&raw)[4]) {
         const int m = task % nvalid, blk = task / nvalid;
         const int ss = blk >> 2, gq = blk & 3;
         float v[32];
-        {
-            const uint16_t* p = src + (int64_t)s_row[m] * K + blk * 32;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(p + c * 8);
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    v[c * 8 + 2 * h] = act_to_f32((uint16_t)(raw[h] & 0xFFFFu), kGather);
-                    v[c * 8 + 2 * h + 1] = act_to_f32((uint16_t)(raw[h] >> 16), kGather);
-                }
+            for (int h = 0; h < 4; ++h) {
+                v[c * 8 + 2 * h] = act_to_f32((uint16_t)(raw[c][h] & 0xFFFFu), kGather);
+                v[c * 8 + 2 * h + 1] = act_to_f32((uint16_t)(raw[c][h] >> 16), kGather);
             }
         }
-        // Hardware K of element n of block gq is 32 gq + n: lanes 16 * (2 (gq & 1) + n / 16)
-        // + m, byte 16 (gq >> 1) + n % 16.
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             float amax = 0.f;
@@ -318,7 +310,45 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
             }
             scales[(ss * NT + t) * 64 + gq * 16 + m] = (uint8_t)(se + 127);
         }
+    };
+    u32x4_t first[4];
+    const int task0 = threadIdx.x;
+    load_task(task0 < ntask ? task0 : ntask - 1, first);   // unconditional: see after_loads
+    // keeps the caller's loads behind these (and in this loop iteration)
+    asm volatile("" ::: "memory");
+    after_loads();
+    // padding: rows past nvalid (all their blocks) and blocks past K -> zeros,
+    // scale 2^0 (disjoint from the live (row, block) entries)
+    for (int task = threadIdx.x; task < 16 * nss * 4; task += blockDim.x) {
+        const int m = task & 15, blk = task >> 4;
+        if (m < nvalid && blk < nblk) continue;
+        const int ss = blk >> 2, gq = blk & 3;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            uint8_t* base = lds + ((size_t)(ss * NT + t) * 64) * 32;
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                *reinterpret_cast<u32x4_t*>(base + (16 * (2 * (gq & 1) + half) + m) * 32 +
+                                            16 * (gq >> 1)) = z;
+            scales[(ss * NT + t) * 64 + gq * 16 + m] = 127;
+        }
     }
+    if (task0 < ntask) convert_task(task0, first);
+    for (int task = task0 + blockDim.x; task < ntask; task += blockDim.x) {
+        u32x4_t raw[4];
+        load_task(task, raw);
+        convert_task(task, raw);
+    }
+}
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wavefront wait for all of its
+// outstanding loads (the load counter does not tell loads from stores).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <int NB>
@@ -359,8 +389,9 @@ __device__ __forceinline__ void fetch_scales(ScaleRegs<NS>& S, const uint8_t* co
 #pragma unroll
         for (int c = 0; c < kScaleChunks; ++c) {
             const int idx = lane + 64 * c;    // 16-byte chunk of the 16 * nblk-byte run
-            S.v[r][c] = u32x4_t{0u, 0u, 0u, 0u};
-            if (idx < nblk) S.v[r][c] = *reinterpret_cast<const u32x4_t*>(run[r] + idx * 16);
+            // unconditional (chunks past the run reload its last one): a load
+            // under a branch makes the compiler's later waits drain the queue
+            S.v[r][c] = *reinterpret_cast<const u32x4_t*>(run[r] + (idx < nblk ? idx : nblk - 1) * 16);
         }
 }
 
@@ -415,11 +446,12 @@ __device__ __forceinline__ void compute_batch(const WBatch<NB>& B, int ss0, int 
 // wait in registers).  Two concurrent row streams per wavefront, 4 MB apart,
 // sustain measurably less HBM bandwidth than one.
 //
-// Block b streams a fixed range of 16-row tiles of expert b / bpe, so its
-// first weight and scale loads are issued at entry, before the routing is
-// read.  The expert's pairs are taken 16 at a time (one pass over the tiles
-// per group of 16; decode steps have one group); blocks of experts without
-// pairs exit after their first prefetch.
+// Block b streams a fixed range of 16-row tiles of expert b / bpe.  It reads
+// the expert's pair range, issues the loads of the first activation rows and
+// only then its first weight batches, so the activation staging overlaps the
+// weight stream instead of queueing behind it.  The expert's pairs are taken
+// 16 at a time (one pass over the tiles per group of 16; decode steps have
+// one group); blocks of experts without pairs exit before loading anything.
 template <bool kGateUp>
 __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
@@ -452,8 +484,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const uint8_t* qe = wq + (size_t)e * (kGateUp ? 2 * F : D) * rowbytes;
     const uint8_t* se = ws + (size_t)e * (kGateUp ? 2 * F : D) * nblk;
 
+    // (a wavefront without tiles prefetches the block's last tile, so every
+    // load is in bounds and unconditional)
+    auto tile_at = [&](int j) { return min(a + wave + j * kStreamWaves, b - 1); };
     auto row_of = [&](int s) {
-        const int tile = a + wave + (s / seg) * kStreamWaves;
+        const int tile = tile_at(s / seg);
         const int r = NS == 1 ? 0 : (s / nbt) % NS;   // up rows follow the F gate rows
         return qe + (size_t)(r * F + tile * 16 + m) * rowbytes;
     };
@@ -473,28 +508,25 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     WBatch<NB> B0, B1, B2;
     ScaleRegs<NS> SR;
     auto prologue = [&]() {
-        if (steps > 0) {
+        {
             const uint8_t* run[NS];
-            runs_of(a + wave, run);
+            runs_of(tile_at(0), run);
             fetch_scales<NS>(SR, run, lane, nblk);
             fetch(B0, 0);
             fetch(B1, 1);
             if constexpr (kRing == 3) fetch(B2, 2);
         }
     };
-    prologue();                                // weights in flight before routing is read
     const int row_beg = offsets[e], ne = offsets[e + 1] - row_beg;
     if (ne <= 0) return;
 
     for (int tg = 0; tg < ne; tg += 16) {
         const int row0 = row_beg + tg;
         const int nvalid = min(16, ne - tg);
-        if (tg > 0) {
-            __syncthreads();                   // previous group's rows no longer read
-            prologue();
-        }
-        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row);
-        __syncthreads();
+        if (tg > 0) __syncthreads();           // previous group's rows no longer read
+        // the weight prefetch goes out right behind the first activation loads
+        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row, prologue);
+        lds_barrier();                         // not __syncthreads: the weight loads stay in flight
 
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc_gate = {0.f, 0.f, 0.f, 0.f};
         // Tile results stay in registers until the wave has issued its last
@@ -521,7 +553,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
                 commit_scales<NS>(SR, wave_sc, lane, nblk);
                 const int nxt = s + seg < steps ? s + seg : s;
                 const uint8_t* run[NS];
-                runs_of(a + wave + (nxt / seg) * kStreamWaves, run);
+                runs_of(tile_at(nxt / seg), run);
                 fetch_scales<NS>(SR, run, lane, nblk);
             }
             const int r = NS == 1 ? 0 : (s / nbt) % NS;
