@@ -107,6 +107,8 @@ def main() -> int:
     ap.add_argument("--workload", default="gptoss20b_decode")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--algo", default="auto", choices=["auto", "stream", "gemm"],
+                    help="expert algorithm (default: the library's automatic choice)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a kernel of known traffic)")
@@ -148,7 +150,9 @@ def main() -> int:
     routing = moe.alloc_routing(cfg.T, cfg.E, cfg.k, dev)
     route_ws = moe.route_workspace(cfg.T, cfg.D, cfg.E, cfg.k, dev)
     mlp_ws = moe.mlp_workspace(cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, dev)
-    layers = [moe.PreparedLayer(xd, wrd, bd, w, cfg.k, out, routing, route_ws, mlp_ws)
+    algo = {"auto": moe.MLP_AUTO, "stream": moe.MLP_STREAM,
+            "gemm": moe.MLP_GROUPED_GEMM}[args.algo]
+    layers = [moe.PreparedLayer(xd, wrd, bd, w, cfg.k, out, routing, route_ws, mlp_ws, algo=algo)
               for w in copies]
     torch.cuda.synchronize()
 
@@ -181,7 +185,8 @@ def main() -> int:
     work = algorithmic_work(cfg, counts)
     # the library's automatic choice: the grouped GEMM once the average expert
     # receives 32 pairs, weight streaming below that
-    decode = cfg.T * cfg.k < 32 * cfg.E
+    decode = (args.algo == "stream" or
+              (args.algo == "auto" and cfg.T * cfg.k < 32 * cfg.E))
     if decode:
         ach = work["gateup_bytes"] / (gateup_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
