@@ -175,8 +175,9 @@ def test_route_shapes(T, D, E, k):
     check_route(x, wr, b, k, "shape T=%d D=%d E=%d k=%d" % (T, D, E, k))
 
 
-def test_route_exact_ties_go_to_lower_id():
-    T, D, E, k = 70, 64, 12, 4
+@pytest.mark.parametrize("T", [70, 40])      # many-token path, and the one-block path (T <= 64)
+def test_route_exact_ties_go_to_lower_id(T):
+    D, E, k = 64, 12, 4
     x = np.zeros((T, D), np.uint16)
     wr = np.ones((E, D), np.float32)
     b = np.array([0.5, 2, 2, 1, 2, 0, 1, 1, 3, 0.5, 2, 3], np.float32)
@@ -186,6 +187,23 @@ def test_route_exact_ties_go_to_lower_id():
     for a, b_ in (("ids", "ids"), ("counts", "counts"), ("offsets", "offsets"),
                   ("sorted_pairs", "sorted"), ("pair_pos", "pos")):
         assert np.array_equal(g[a], ref[b_]), a
+
+
+# The one-block routing kernel (T <= 64 and T*E <= 8192) is compiled once per
+# k: every k, expert counts that leave wavefronts without experts (E < 16)
+# or give them several, and both sides of its size limits.
+SMALL_ROUTE = ([(64, 64, 2 * k + 3, k) for k in range(1, 9)] +
+               [(17, 96, 128, 3), (32, 64, 256, 7), (64, 64, 128, 6),    # T*E = 8192
+                (64, 64, 129, 5), (65, 64, 8, 2), (33, 2880, 200, 8)])
+
+
+@pytest.mark.parametrize("T,D,E,k", SMALL_ROUTE)
+def test_route_small_batches(T, D, E, k):
+    rng = np.random.default_rng(1000 + T * 3 + E * 5 + k)
+    x = MI.f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    wr = (rng.standard_normal((E, D)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    check_route(x, wr, b, k, "small-batch T=%d D=%d E=%d k=%d" % (T, D, E, k))
 
 
 # ------------------------------------------------------------------ full layer
