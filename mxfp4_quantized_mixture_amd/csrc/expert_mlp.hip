@@ -247,19 +247,29 @@ __device__ __forceinline__ float act_to_f32(uint16_t v, bool is_bf16) {
                    : (float)__builtin_bit_cast(_Float16, v);
 }
 
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wavefront wait for all of its
+// outstanding loads (the load counter does not tell loads from stores).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Stage the unit's rows (pairs row0 .. row0 + nvalid - 1 in sorted order;
 // gathered bf16 x rows for gate/up, contiguous fp16 h rows for down) as NT
 // fp8 terms.  One thread per (row, 32-element block); rows past nvalid and
 // blocks past K are zero with scale 2^0.
 //
 // after_loads() runs once every thread has issued the loads of its first
-// (row, block): the caller issues its weight prefetch there.  Loads complete
-// in issue order as far as the wait counter is concerned, so activation
-// loads issued behind a chip-wide weight prefetch would wait for all of it.
-template <int NT, bool kGather, typename F>
+// (row, block), after_convert() once it has converted it: the caller issues
+// its weight prefetch there.  Loads complete in issue order as far as the
+// wait counter is concerned, so activation loads issued behind a chip-wide
+// weight prefetch would wait for all of it.
+template <int NT, bool kGather, typename F, typename G>
 __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __restrict__ sorted,
                             int row0, int nvalid, int k, int K, uint8_t* lds, int* s_row,
-                            F&& after_loads) {
+                            F&& after_loads, G&& after_convert) {
     if (threadIdx.x < 16)
         s_row[threadIdx.x] = threadIdx.x < nvalid
             ? (kGather ? sorted[row0 + threadIdx.x] / k : row0 + threadIdx.x) : -1;
@@ -316,6 +326,12 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
     load_task(task0 < ntask ? task0 : ntask - 1, first);   // unconditional: see after_loads
     // keeps the caller's loads behind these (and in this loop iteration)
     asm volatile("" ::: "memory");
+    // No wavefront issues weight loads before every wavefront has issued its
+    // activation loads: the CU's memory pipeline serves requests roughly in
+    // issue order, so a late wavefront's activation loads would otherwise
+    // queue behind the other wavefronts' prefetches.  (Orders issue only:
+    // nothing here waits for a load.)
+    lds_barrier();
     after_loads();
     // padding: rows past nvalid (all their blocks) and blocks past K -> zeros,
     // scale 2^0 (disjoint from the live (row, block) entries)
@@ -335,20 +351,12 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
         }
     }
     if (task0 < ntask) convert_task(task0, first);
+    after_convert();
     for (int task = task0 + blockDim.x; task < ntask; task += blockDim.x) {
         u32x4_t raw[4];
         load_task(task, raw);
         convert_task(task, raw);
     }
-}
-
-// Workgroup barrier ordering LDS accesses only.  __syncthreads() also
-// orders global memory, which makes every wavefront wait for all of its
-// outstanding loads (the load counter does not tell loads from stores).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <int NB>
@@ -507,15 +515,19 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     };
     WBatch<NB> B0, B1, B2;
     ScaleRegs<NS> SR;
-    auto prologue = [&]() {
-        {
-            const uint8_t* run[NS];
-            runs_of(tile_at(0), run);
-            fetch_scales<NS>(SR, run, lane, nblk);
-            fetch(B0, 0);
-            fetch(B1, 1);
-            if constexpr (kRing == 3) fetch(B2, 2);
-        }
+    // The first tile's scales and weight batch go out with the activation
+    // loads; the rest of the ring once this wavefront has converted its
+    // first activation block (a wavefront issuing its whole ring first stalls
+    // in load issue and holds up the staging barrier).
+    auto prologue_a = [&]() {
+        const uint8_t* run[NS];
+        runs_of(tile_at(0), run);
+        fetch_scales<NS>(SR, run, lane, nblk);
+        fetch(B0, 0);
+    };
+    auto prologue_b = [&]() {
+        fetch(B1, 1);
+        if constexpr (kRing == 3) fetch(B2, 2);
     };
     const int row_beg = offsets[e], ne = offsets[e + 1] - row_beg;
     if (ne <= 0) return;
@@ -525,7 +537,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
         const int nvalid = min(16, ne - tg);
         if (tg > 0) __syncthreads();           // previous group's rows no longer read
         // the weight prefetch goes out right behind the first activation loads
-        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row, prologue);
+        stage_split<NT, kGateUp>(act, sorted, row0, nvalid, k, K, lds_stage, s_row, prologue_a,
+                                 prologue_b);
         lds_barrier();                         // not __syncthreads: the weight loads stay in flight
 
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc_gate = {0.f, 0.f, 0.f, 0.f};
