@@ -33,11 +33,19 @@
  *  - The shared scale is an E8M0 byte b meaning 2^(b-127); b = 255 (NaN) is
  *    never produced.
  *  - Scale rule 0: s = floor(log2(amax / 6)); rule 1 (OCP MX v1.0):
- *    s = floor(log2(amax)) - 2.  s is clamped to [-127, 127]; amax = 0 gives
- *    s = -127.
+ *    s = floor(log2(amax)) - 2; rule 2: s = ceil(log2(amax / 6)), the
+ *    smallest scale at which no element exceeds 6 (so stochastic rounding
+ *    never saturates).  s is clamped to [-127, 127]; amax = 0 gives s = -127.
  *  - Element encode: round to nearest E2M1 value, ties to the even code,
  *    saturate at +-6, keep the sign bit (so -0 and negatives that round to
  *    zero give code 0x8).
+ *  - Stochastic rounding (the training recipe "MXFP4 기반 MoE 기술 리뷰"
+ *    section 2 cites, with no details): between the neighbouring E2M1 values
+ *    lo <= |y| < hi, hi is taken with probability (|y| - lo) / (hi - lo), so
+ *    the expected value is |y|.  The draw for element i = row * K + col is
+ *    output i + 1 of a SplitMix64 generator whose state starts at the seed,
+ *    its top 24 bits as an integer u; hi is taken when u < 2^24 (|y| - lo) /
+ *    (hi - lo).
  *  - Packing: byte i of a row holds element 2i in its low nibble and element
  *    2i+1 in its high nibble; blocks run along the contraction dimension.
  *  - Router: logits = x . Wr^T + b (a linear layer with bias).
@@ -104,8 +112,20 @@ static int floor_log2_ratio(double amax, double c)
     return s;
 }
 
+/* Smallest integer s with amax <= c * 2^s (= ceil(log2(amax / c))), exactly. */
+static int ceil_log2_ratio(double amax, double c)
+{
+    int s = (int)ceil(log2(amax / c));
+    while (ldexp(c, s - 1) >= amax)
+        --s;
+    while (ldexp(c, s) < amax)
+        ++s;
+    return s;
+}
+
 /* Shared block exponent s from the block's largest magnitude.
- * rule 0: s = floor(log2(amax / 6)); rule 1 (OCP MX): floor(log2 amax) - 2. */
+ * rule 0: s = floor(log2(amax / 6)); rule 1 (OCP MX): floor(log2 amax) - 2;
+ * rule 2: s = ceil(log2(amax / 6)). */
 int oracle_scale_exponent(double amax, int rule)
 {
     int s;
@@ -113,8 +133,10 @@ int oracle_scale_exponent(double amax, int rule)
         return -127;
     if (rule == 0)
         s = floor_log2_ratio(amax, 6.0);
-    else
+    else if (rule == 1)
         s = floor_log2_ratio(amax, 1.0) - 2;
+    else
+        s = ceil_log2_ratio(amax, 6.0);
     if (s < -127)
         s = -127;
     if (s > 127)
@@ -163,16 +185,58 @@ int oracle_e2m1_encode(double y)
     return e2m1_encode_grid(y, grid);
 }
 
+/* SplitMix64, output n >= 1 of the generator whose state starts at `seed`:
+ * the state advances by the golden-ratio increment 0x9E3779B97F4A7C15 and
+ * each output is the state through the mixing function of the JDK's
+ * java.util.SplittableRandom (mix64; the same constants as S. Vigna's
+ * public-domain splitmix64.c). */
+uint64_t oracle_splitmix64(uint64_t seed, uint64_t n)
+{
+    uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* Stochastic rounding of an already-scaled y with the draw u in [0, 2^24):
+ * between the neighbouring values grid[c] <= |y| < grid[c + 1], the upper one
+ * is taken when u < 2^24 (|y| - grid[c]) / (grid[c + 1] - grid[c]) (every
+ * quantity here is exact in fp64); |y| >= 6 saturates; sign kept. */
+static int e2m1_encode_stochastic(double y, uint32_t u, const double grid[8])
+{
+    int sign = signbit(y) ? 1 : 0;
+    double a = fabs(y);
+    int c = 7;
+    if (a < grid[7]) {
+        c = 0;
+        while (grid[c + 1] <= a)
+            ++c;
+        double frac = (a - grid[c]) / (grid[c + 1] - grid[c]);
+        if ((double)u < ldexp(frac, 24))
+            ++c;
+    }
+    return (sign << 3) | c;
+}
+
+int oracle_e2m1_encode_stochastic(double y, uint32_t u)
+{
+    double grid[8];
+    e2m1_grid(grid);
+    return e2m1_encode_stochastic(y, u, grid);
+}
+
 /* ------------------------------------------------------------------------ */
 /* MXFP4 quantize / dequantize                                               */
 /* ------------------------------------------------------------------------ */
 
 /* w: bf16 bits [rows, K]; q: [rows, K/2] packed codes; s: [rows, K/32] E8M0.
- * Returns 0, or -1 if K is not a multiple of 32 or the rule is unknown. */
-int oracle_quantize(const uint16_t *w, int64_t rows, int64_t K, int rule,
-                    uint8_t *q, uint8_t *s)
+ * rounding 0: nearest even; 1: stochastic with the given seed.
+ * Returns 0, or -1 if K is not a multiple of 32 or the rule or rounding is
+ * unknown. */
+int oracle_quantize_ex(const uint16_t *w, int64_t rows, int64_t K, int rule,
+                       int rounding, uint64_t seed, uint8_t *q, uint8_t *s)
 {
-    if (K % 32 != 0 || (rule != 0 && rule != 1))
+    if (K % 32 != 0 || rule < 0 || rule > 2 || rounding < 0 || rounding > 1)
         return -1;
     int64_t nblk = K / 32;
     double grid[8];
@@ -190,14 +254,28 @@ int oracle_quantize(const uint16_t *w, int64_t rows, int64_t K, int rule,
             s[r * nblk + b] = (uint8_t)(se + 127);
             double inv_scale = ldexp(1.0, -se);   /* 2^-s: products are exact */
             int codes[32];
-            for (int i = 0; i < 32; ++i)
-                codes[i] = e2m1_encode_grid(oracle_bf16_to_double(blk[i]) * inv_scale, grid);
+            for (int i = 0; i < 32; ++i) {
+                double y = oracle_bf16_to_double(blk[i]) * inv_scale;
+                if (rounding == 0) {
+                    codes[i] = e2m1_encode_grid(y, grid);
+                } else {
+                    uint64_t idx = (uint64_t)(r * K + b * 32 + i);
+                    uint32_t u = (uint32_t)(oracle_splitmix64(seed, idx + 1) >> 40);
+                    codes[i] = e2m1_encode_stochastic(y, u, grid);
+                }
+            }
             uint8_t *qb = q + r * (K / 2) + b * 16;
             for (int i = 0; i < 16; ++i)
                 qb[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
         }
     }
     return 0;
+}
+
+int oracle_quantize(const uint16_t *w, int64_t rows, int64_t K, int rule,
+                    uint8_t *q, uint8_t *s)
+{
+    return oracle_quantize_ex(w, rows, K, rule, 0, 0, q, s);
 }
 
 /* Element (r, c) of a packed MXFP4 matrix with K columns, as a double. */

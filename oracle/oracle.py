@@ -52,6 +52,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_e2m1_encode.restype = i32
         L.oracle_quantize.argtypes = [P, i64, i64, i32, P, P]
         L.oracle_quantize.restype = i32
+        L.oracle_quantize_ex.argtypes = [P, i64, i64, i32, i32, ctypes.c_uint64, P, P]
+        L.oracle_quantize_ex.restype = i32
+        L.oracle_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.oracle_splitmix64.restype = ctypes.c_uint64
+        L.oracle_e2m1_encode_stochastic.argtypes = [f64, ctypes.c_uint32]
+        L.oracle_e2m1_encode_stochastic.restype = i32
         L.oracle_dequantize.argtypes = [P, P, i64, i64, P]
         L.oracle_dequantize.restype = None
         L.oracle_route.argtypes = [P, P, P, i32, i32, i32, i32,
@@ -92,16 +98,29 @@ def e2m1_encode(y: float) -> int:
     return lib().oracle_e2m1_encode(float(y))
 
 
+def e2m1_encode_stochastic(y: float, u: int) -> int:
+    """Stochastic E2M1 code of an already-scaled y with the 24-bit draw u."""
+    return lib().oracle_e2m1_encode_stochastic(float(y), int(u))
+
+
+def splitmix64(seed: int, n: int) -> int:
+    """Output n >= 1 of the SplitMix64 generator whose state starts at seed."""
+    return lib().oracle_splitmix64(int(seed) & (2**64 - 1), int(n) & (2**64 - 1))
+
+
 # -- MXFP4 -----------------------------------------------------------------
 
-def quantize(w_bf16: np.ndarray, rule: int = 0) -> tuple[np.ndarray, np.ndarray]:
-    """bf16 bits [..., K] -> (packed codes [..., K/2], E8M0 scales [..., K/32])."""
+def quantize(w_bf16: np.ndarray, rule: int = 0, stochastic: bool = False,
+             seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [..., K] -> (packed codes [..., K/2], E8M0 scales [..., K/32]).
+    stochastic: stochastic rounding with the SplitMix64 stream of `seed`."""
     w = _c(w_bf16, np.uint16)
     K = w.shape[-1]
     rows = w.size // K
     q = np.empty(w.shape[:-1] + (K // 2,), dtype=np.uint8)
     s = np.empty(w.shape[:-1] + (K // 32,), dtype=np.uint8)
-    rc = lib().oracle_quantize(_ptr(w), rows, K, rule, _ptr(q), _ptr(s))
+    rc = lib().oracle_quantize_ex(_ptr(w), rows, K, rule, 1 if stochastic else 0,
+                                  int(seed) & (2**64 - 1), _ptr(q), _ptr(s))
     if rc != 0:
         raise ValueError("oracle_quantize rejected its arguments (rc=%d)" % rc)
     return q, s

@@ -71,13 +71,20 @@ def scale_exponent_from_bits(amax_bits: int, rule: int) -> int:
     log2((1+M/128)/6) lies in [-3, -2) when M < 64 (1+m < 1.5) and in
     [-2, -1) otherwise, so s = E - 130 + [M >= 64].
     rule 1, floor(log2 amax) - 2 = E - 127 - 2.
-    A subnormal or zero maximum lies below 2^-126, so both rules give a value
+    rule 2, ceil(log2(amax/6)): log2((1+M/128)/1.5) lies in (-1, 0] when
+    M <= 64 and in (0, 1) otherwise, so s = E - 129 + [M > 64].
+    A subnormal or zero maximum lies below 2^-126, so every rule gives a value
     under -127, clamped to -127.  Results are clamped to [-127, 127].
     """
     _, E, M = bf16_fields(amax_bits)
     if E == 0:
         return -127
-    s = (E - 130 + (1 if M >= 64 else 0)) if rule == 0 else (E - 129)
+    if rule == 0:
+        s = E - 130 + (1 if M >= 64 else 0)
+    elif rule == 1:
+        s = E - 129
+    else:
+        s = E - 129 + (1 if M > 64 else 0)
     return max(-127, min(127, s))
 
 
