@@ -99,6 +99,35 @@ def cpu_baseline(cfg, inp, tokens) -> dict:
             "sample": what, "seconds": dt, "host_cpu": platform.processor() or platform.machine()}
 
 
+def bench_quantize(cfg, args, moe, torch, dev) -> int:
+    """mxfp4_quantize on the workload's W13 (E * 2F rows of D bf16), both
+    roundings; HBM bytes = 2 B read per element + 0.5 + 1/32 B written."""
+    from synth import moe_inputs as MI
+    w13, _ = MI.gen_experts(cfg, args.seed, threads=16)
+    w = torch.from_numpy(w13.reshape(-1, cfg.D).view(np.int16)).to(dev).view(torch.bfloat16)
+    rows, K = w.shape
+    nbytes = rows * K * 2 + rows * K // 2 + rows * K // 32
+    out = {}
+    for name, kw in (("nearest_even", {}), ("stochastic", {"stochastic": True, "seed": 1})):
+        for _ in range(max(args.warmup // 10, 2)):
+            moe.mxfp4_quantize(w, moe.SCALE_CEIL_DIV6 if kw else moe.SCALE_FLOOR_DIV6, **kw)
+        n = max(args.steps // 20, 5)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(n):
+            moe.mxfp4_quantize(w, moe.SCALE_CEIL_DIV6 if kw else moe.SCALE_FLOOR_DIV6, **kw)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / n
+        out[name] = {"ms": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    print(json.dumps({"metric": "mxfp4_quantize HBM GB/s", "workload": cfg.name + " W13",
+                      "rows": rows, "K": K, "bytes_per_call": nbytes, "calls": n,
+                      "results": out}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +138,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algo", default="auto", choices=["auto", "stream", "gemm"],
                     help="expert algorithm (default: the library's automatic choice)")
+    ap.add_argument("--quantize", action="store_true",
+                    help="time mxfp4_quantize (nearest-even and stochastic rounding) on the "
+                         "workload's W13 instead of the layer")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a kernel of known traffic)")
@@ -134,6 +166,8 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes": nbytes, "dispatches": 5}), flush=True)
         return 0
     cfg = MI.CONFIGS[args.workload]
+    if args.quantize:
+        return bench_quantize(cfg, args, moe, torch, dev)
     wr, b = MI.gen_router(cfg, args.seed)
     x = MI.gen_x(cfg, args.seed)
     w13, w2 = MI.gen_experts(cfg, args.seed, threads=16)

@@ -65,8 +65,16 @@ typedef enum {
 typedef enum {
     MXFP4_SCALE_FLOOR_DIV6 = 0, /* s = floor(log2(amax / 6)): the block maximum
                                    scales into [6, 12) and saturates to 6 */
-    MXFP4_SCALE_OCP = 1         /* s = floor(log2(amax)) - 2 (OCP MX v1.0) */
+    MXFP4_SCALE_OCP = 1,        /* s = floor(log2(amax)) - 2 (OCP MX v1.0) */
+    MXFP4_SCALE_CEIL_DIV6 = 2   /* s = ceil(log2(amax / 6)): the smallest scale
+                                   at which no element exceeds 6 */
 } mxfp4_scale_rule_t;
+
+/* Element rounding of mxfp4_quantize_ex. */
+typedef enum {
+    MXFP4_ROUND_NEAREST_EVEN = 0,
+    MXFP4_ROUND_STOCHASTIC = 1  /* see mxfp4_quantize_ex */
+} mxfp4_rounding_t;
 
 /* How moe_expert_mlp_ex runs the experts (moe_expert_mlp: automatic). */
 typedef enum {
@@ -101,6 +109,24 @@ MOE_API int moe_abi_version(void);
 MOE_API moe_status_t mxfp4_quantize(const uint16_t *w, int64_t rows, int64_t K,
                             int scale_rule, uint8_t *q, uint8_t *s,
                             hipStream_t stream);
+
+/*
+ * mxfp4_quantize_ex -- mxfp4_quantize with the element rounding chosen.
+ * MXFP4_ROUND_STOCHASTIC (the stochastic-rounding training recipe cited in
+ * "MXFP4 기반 MoE (Mixture-of-Experts) 기술 리뷰", section 2; the pages give
+ * no details, the reading here): element i = row * K + col, scaled to
+ * y = v * 2^-s, takes the upper of its two neighbouring E2M1 values
+ * lo <= |y| < hi when u < 2^24 (|y| - lo) / (hi - lo), else the lower one,
+ * where u is the top 24 bits of output i + 1 of a SplitMix64 generator whose
+ * state starts at `seed` (state += 0x9E3779B97F4A7C15, output = the mix64
+ * finalizer of java.util.SplittableRandom); |y| >= 6 saturates; sign kept.
+ * With MXFP4_SCALE_CEIL_DIV6 no element saturates, so the expected
+ * dequantized value equals the input.  The same seed gives the same codes.
+ * Errors as for mxfp4_quantize (MOE_ERR_ENUM also for an unknown rounding).
+ */
+MOE_API moe_status_t mxfp4_quantize_ex(const uint16_t *w, int64_t rows, int64_t K,
+                            int scale_rule, int rounding, uint64_t seed,
+                            uint8_t *q, uint8_t *s, hipStream_t stream);
 
 /*
  * mxfp4_dequantize -- MXFP4 to bf16 (exact for every scale byte in

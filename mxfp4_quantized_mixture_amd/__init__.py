@@ -25,12 +25,14 @@ import torch
 
 __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "moe_route", "moe_expert_mlp",
            "Routing", "ExpertWeights", "MoELayer", "MoEError", "lib",
-           "SCALE_FLOOR_DIV6", "SCALE_OCP", "MLP_AUTO", "MLP_STREAM", "MLP_GROUPED_GEMM",
-           "LIB_PATH"]
+           "SCALE_FLOOR_DIV6", "SCALE_OCP", "SCALE_CEIL_DIV6", "ROUND_NEAREST_EVEN",
+           "ROUND_STOCHASTIC", "MLP_AUTO", "MLP_STREAM", "MLP_GROUPED_GEMM", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
 SCALE_FLOOR_DIV6 = 0
 SCALE_OCP = 1
+SCALE_CEIL_DIV6 = 2
+ROUND_NEAREST_EVEN, ROUND_STOCHASTIC = 0, 1
 MLP_AUTO, MLP_STREAM, MLP_GROUPED_GEMM = 0, 1, 2
 
 
@@ -60,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.moe_abi_version.restype = ctypes.c_int
         L.mxfp4_quantize.argtypes = [P, i64, i64, ctypes.c_int, P, P, P]
         L.mxfp4_quantize.restype = ctypes.c_int
+        L.mxfp4_quantize_ex.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_uint64, P, P, P]
+        L.mxfp4_quantize_ex.restype = ctypes.c_int
         L.mxfp4_dequantize.argtypes = [P, P, i64, i64, P, P]
         L.mxfp4_dequantize.restype = ctypes.c_int
         L.moe_route_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -99,14 +104,17 @@ def _check(fn: str, status: int) -> None:
 
 # ---------------------------------------------------------------- codec
 
-def mxfp4_quantize(w: torch.Tensor, rule: int = SCALE_FLOOR_DIV6):
-    """bf16 [..., K] -> (codes uint8 [..., K/2], E8M0 scales uint8 [..., K/32])."""
+def mxfp4_quantize(w: torch.Tensor, rule: int = SCALE_FLOOR_DIV6, stochastic: bool = False,
+                   seed: int = 0):
+    """bf16 [..., K] -> (codes uint8 [..., K/2], E8M0 scales uint8 [..., K/32]).
+    stochastic: stochastic rounding drawn from the SplitMix64 stream of `seed`."""
     K = w.shape[-1]
     rows = w.numel() // K if K else 0
     q = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
     s = torch.empty(*w.shape[:-1], K // 32, dtype=torch.uint8, device=w.device)
-    _check("mxfp4_quantize", lib().mxfp4_quantize(
-        _dev(w, "w", torch.bfloat16), rows, K, rule, _dev(q, "q"), _dev(s, "s"),
+    _check("mxfp4_quantize", lib().mxfp4_quantize_ex(
+        _dev(w, "w", torch.bfloat16), rows, K, rule, ROUND_STOCHASTIC if stochastic else
+        ROUND_NEAREST_EVEN, int(seed) & (2**64 - 1), _dev(q, "q"), _dev(s, "s"),
         _stream(w.device)))
     return q, s
 

@@ -35,14 +35,24 @@ const char* moe_status_string(int status) {
 
 int moe_abi_version(void) { return 1; }
 
-moe_status_t mxfp4_quantize(const uint16_t* w, int64_t rows, int64_t K, int scale_rule,
-                            uint8_t* q, uint8_t* s, hipStream_t stream) {
+moe_status_t mxfp4_quantize_ex(const uint16_t* w, int64_t rows, int64_t K, int scale_rule,
+                               int rounding, uint64_t seed, uint8_t* q, uint8_t* s,
+                               hipStream_t stream) {
     if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
-    if (scale_rule != MXFP4_SCALE_FLOOR_DIV6 && scale_rule != MXFP4_SCALE_OCP) return MOE_ERR_ENUM;
+    if (scale_rule != MXFP4_SCALE_FLOOR_DIV6 && scale_rule != MXFP4_SCALE_OCP &&
+        scale_rule != MXFP4_SCALE_CEIL_DIV6)
+        return MOE_ERR_ENUM;
+    if (rounding != MXFP4_ROUND_NEAREST_EVEN && rounding != MXFP4_ROUND_STOCHASTIC)
+        return MOE_ERR_ENUM;
     if (rows == 0) return MOE_OK;
     if (!w || !q || !s) return MOE_ERR_NULL;
     if (!aligned16(w) || !aligned16(q)) return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_quantize(w, rows, K, scale_rule, q, s, stream));
+    return hip_status(moe::launch_quantize(w, rows, K, scale_rule, rounding, seed, q, s, stream));
+}
+
+moe_status_t mxfp4_quantize(const uint16_t* w, int64_t rows, int64_t K, int scale_rule,
+                            uint8_t* q, uint8_t* s, hipStream_t stream) {
+    return mxfp4_quantize_ex(w, rows, K, scale_rule, MXFP4_ROUND_NEAREST_EVEN, 0, q, s, stream);
 }
 
 moe_status_t mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,

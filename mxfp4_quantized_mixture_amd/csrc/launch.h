@@ -7,8 +7,8 @@
 
 namespace moe {
 
-hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule,
-                           uint8_t* q, uint8_t* s, hipStream_t stream);
+hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule, int rounding,
+                           uint64_t seed, uint8_t* q, uint8_t* s, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
                              uint16_t* out, hipStream_t stream);
 

@@ -5,9 +5,11 @@
 // with transformers", section 6; "Transformers 4.40 のパフォーマンス向上",
 // section "MXFP4 とは"; OCP MX named in "MXFP4 기반 MoE 기술 리뷰", section 1).
 //
-// The encoder works on the bf16 bit fields with integer arithmetic only, so
-// no floating-point rounding mode, denormal flushing or fast-math setting can
-// change a code.
+// The scale rules and the stochastic encoder work on the bf16 bit fields
+// with integer arithmetic; the nearest-even encoder uses fp32 products that
+// are exact (see e2m1_encode_f32).  The element rounding of the stochastic
+// encoder follows the reading of the stochastic-rounding recipe that "MXFP4
+// 기반 MoE 기술 리뷰" section 2 cites (details in the header).
 #include "device_common.h"
 #include "launch.h"
 
@@ -18,71 +20,153 @@ namespace moe {
 //   amax = (128 + M) * 2^(E - 134) for E > 0.
 //   rule 0: s = floor(log2(amax / 6)) = E - 130 + [M >= 64]   (1 + M/128 >= 1.5)
 //   rule 1: s = floor(log2(amax)) - 2 = E - 129
+//   rule 2: s = ceil(log2(amax / 6))  = E - 129 + [M > 64]    (no element beyond 6)
 // A zero or subnormal maximum lies below 2^-126 and gives s < -127: clamp.
 __device__ __forceinline__ int block_scale_exponent(uint32_t amax_bits, int rule) {
     int E = (int)(amax_bits >> 7);
     int M = (int)(amax_bits & 0x7F);
     if (E == 0) return -127;
-    int s = rule == 0 ? E - 130 + (M >= 64 ? 1 : 0) : E - 129;
+    int s = rule == 0 ? E - 130 + (M >= 64 ? 1 : 0)
+                      : rule == 1 ? E - 129 : E - 129 + (M > 64 ? 1 : 0);
     return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
-// E2M1 code of the bf16 value v scaled by 2^-s: nearest of
-// {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating; sign kept.
-// With |v| = sig * 2^e2, 4|v|/2^s = sig * 2^(e2 - s + 2) is compared against
-// the doubled midpoints {1,3,5,7,10,14,20} of the grid in quarter units,
-// carrying a sticky bit for the shifted-out fraction.
-__device__ __forceinline__ uint32_t e2m1_encode(uint32_t v, int s) {
-    uint32_t sign = (v >> 15) & 1u;
-    uint32_t E = (v >> 7) & 0xFFu;
-    uint32_t M = v & 0x7Fu;
-    uint32_t sig = E ? (M | 0x80u) : M;
-    int e2 = (E ? (int)E : 1) - 134;
-    int sh = e2 - s + 2;
-    uint32_t v2;  // 2 * (4y), plus 1 if any fraction bit was dropped
-    if (sig == 0) {
-        v2 = 0;
-    } else if (sh >= 0) {
-        v2 = sh >= 6 ? 0xFFFFu : (sig << sh) << 1;
+// E2M1 code of the bf16 value v scaled by 2^-s: nearest of {0, .5, 1, 1.5,
+// 2, 3, 4, 6}, ties to the even code, saturating; sign kept (so -0 and
+// negatives that round to zero give 0x8).  y = |v| * 2^-s is exact
+// here (a power-of-two multiple of a bf16 value; when it is too small for
+// that it lies far below 0.25 and rounds to 0 either way; s <= 126 for any
+// finite bf16 maximum, so 2^-s is a normal fp32), and on each binade of the
+// grid the nearest code is one round-half-even: 2y below 2 (0, .5, 1, 1.5,
+// 2 are 0..4), y + 2 below 4 (2, 3, 4 are codes 4..6), y / 2 + 4 below 6
+// (4, 6 are codes 6, 7); ties go to the even integer, which is the code
+// with mantissa bit 0.  Saturates at 6 (including an infinite product).
+__device__ __forceinline__ uint32_t e2m1_encode_f32(uint32_t v, float inv_scale) {
+    const float y = __builtin_bit_cast(float, (v & 0x7FFFu) << 16) * inv_scale;
+    float c;
+    if (y < 2.0f)
+        c = __builtin_rintf(2.0f * y);
+    else if (y < 4.0f)
+        c = __builtin_rintf(y) + 2.0f;
+    else if (y < 6.0f)
+        c = __builtin_rintf(0.5f * y) + 4.0f;
+    else
+        c = 7.0f;
+    return ((v >> 12) & 8u) | (uint32_t)c;
+}
+
+// SplitMix64: output n >= 1 of the generator whose state starts at `seed`
+// (state += 0x9E3779B97F4A7C15 per output; output = the mix64 finalizer of
+// java.util.SplittableRandom, also S. Vigna's splitmix64.c).
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
+    uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Stochastic E2M1 code of the bf16 value v scaled by 2^-s, with the draw u in
+// [0, 2^24): between the neighbouring grid values lo <= |y| < hi the upper
+// one is taken when u < 2^24 (|y| - lo) / (hi - lo); |y| >= 6 saturates; sign
+// kept.  Integer form: Y = ceil(4|y| 2^40), in quarter units with 40 fraction
+// bits (exact unless 4|y| < 2^-40); the grid {0, 2, 4, 6, 8, 12, 16, 24}
+// has steps 2, 4, 8; the threshold ceil((Y - lo) / step * 2^-16) equals
+// ceil(2^24 (|y| - lo) / (hi - lo)), and u < x <=> u < ceil(x) for integer u.
+__device__ __forceinline__ uint32_t e2m1_encode_stochastic(uint32_t v, int s, uint32_t u) {
+    const uint32_t sign = (v >> 15) & 1u;
+    const uint32_t E = (v >> 7) & 0xFFu;
+    const uint32_t M = v & 0x7Fu;
+    const uint32_t sig = E ? (M | 0x80u) : M;
+    if (sig == 0) return sign << 3;
+    const int sh = (E ? (int)E : 1) - 134 - s + 2;       // 4|y| = sig * 2^sh
+    if (sh >= 6) return (sign << 3) | 7u;                 // 4|y| >= 64
+    const int t = sh + 40;
+    uint64_t Y;
+    if (t >= 0) {
+        Y = (uint64_t)sig << t;
     } else {
-        int n = -sh > 9 ? 9 : -sh;
-        uint32_t qi = sig >> n;
-        uint32_t sticky = (sig & ((1u << n) - 1u)) != 0u;
-        v2 = (qi << 1) | sticky;
+        const int n = -t > 63 ? 63 : -t;
+        Y = ((uint64_t)sig >> n) + (((uint64_t)sig & ((1ull << n) - 1ull)) != 0ull);
     }
-    uint32_t c = (v2 > 2u) + (v2 >= 6u) + (v2 > 10u) + (v2 >= 14u) +
-                 (v2 > 20u) + (v2 >= 28u) + (v2 > 40u);
-    return (sign << 3) | c;
+    const uint64_t one = 1ull << 40;
+    if (Y >= 24 * one) return (sign << 3) | 7u;
+    uint32_t c;
+    uint64_t lo;
+    int n;                                                // 16 + log2(step)
+    if (Y < 8 * one) {
+        c = (uint32_t)(Y >> 41);
+        lo = (uint64_t)c << 41;
+        n = 17;
+    } else if (Y < 16 * one) {
+        c = 4u + (uint32_t)((Y - 8 * one) >> 42);
+        lo = 8 * one + ((uint64_t)(c - 4u) << 42);
+        n = 18;
+    } else {
+        c = 6u;
+        lo = 16 * one;
+        n = 19;
+    }
+    const uint64_t d = Y - lo;
+    const uint64_t thr = (d >> n) + ((d & ((1ull << n) - 1ull)) != 0ull);
+    return (sign << 3) | (c + ((uint64_t)u < thr ? 1u : 0u));
 }
 
 // Four lanes per 32-element block; each lane owns 8 consecutive elements
 // (one 16-byte load), so a wavefront reads 1 KiB of contiguous bf16 and writes
-// 256 contiguous bytes of codes.
+// 256 contiguous bytes of codes.  Each thread takes kQuantUnroll grid strides
+// at once, all their loads issued before any is encoded (one load in flight
+// per thread leaves HBM idle between round trips).
+// (stochastic: element e = 8 i + m of the flattened [rows, K] matrix draws
+// the top 24 bits of SplitMix64 output e + 1)
+constexpr int kQuantUnroll = 4;
+
+template <bool kStochastic>
 __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ s, int64_t nquads, int rule) {
+    uint8_t* __restrict__ s, int64_t nquads, int rule, uint64_t seed) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nquads; i += stride) {
+    for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < nquads;
+         i0 += kQuantUnroll * stride) {
         // nquads is a multiple of 4 and stride of 256, so the four lanes of a
-        // block are always active together for the shuffles below.
-        u32x4_t raw = *reinterpret_cast<const u32x4_t*>(w + i * 8);
-        uint32_t amax = 0;
+        // block are always active (or idle) together for the shuffles below.
+        u32x4_t raw[kQuantUnroll];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t lo = raw[j] & 0x7FFFu, hi = (raw[j] >> 16) & 0x7FFFu;
-            amax = max(amax, max(lo, hi));
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            const int64_t i = i0 + u * stride;
+            raw[u] = i < nquads ? *reinterpret_cast<const u32x4_t*>(w + i * 8)
+                                : u32x4_t{0u, 0u, 0u, 0u};
         }
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-        const int se = block_scale_exponent(amax, rule);
-        uint32_t codes = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            codes |= e2m1_encode(raw[j] & 0xFFFFu, se) << (8 * j);
-            codes |= e2m1_encode(raw[j] >> 16, se) << (8 * j + 4);
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            const int64_t i = i0 + u * stride;
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t lo = raw[u][j] & 0x7FFFu, hi = (raw[u][j] >> 16) & 0x7FFFu;
+                amax = max(amax, max(lo, hi));
+            }
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+            if (i >= nquads) continue;
+            const int se = block_scale_exponent(amax, rule);
+            uint32_t codes = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (kStochastic) {
+                    const uint64_t e0 = (uint64_t)i * 8 + 2 * j;
+                    const uint32_t u0 = (uint32_t)(splitmix64(seed, e0 + 1) >> 40);
+                    const uint32_t u1 = (uint32_t)(splitmix64(seed, e0 + 2) >> 40);
+                    codes |= e2m1_encode_stochastic(raw[u][j] & 0xFFFFu, se, u0) << (8 * j);
+                    codes |= e2m1_encode_stochastic(raw[u][j] >> 16, se, u1) << (8 * j + 4);
+                } else {
+                    const float inv = exp2i_neg(se);
+                    codes |= e2m1_encode_f32(raw[u][j] & 0xFFFFu, inv) << (8 * j);
+                    codes |= e2m1_encode_f32(raw[u][j] >> 16, inv) << (8 * j + 4);
+                }
+            }
+            reinterpret_cast<uint32_t*>(q)[i] = codes;
+            if ((i & 3) == 0) s[i >> 2] = (uint8_t)(se + 127);
         }
-        reinterpret_cast<uint32_t*>(q)[i] = codes;
-        if ((i & 3) == 0) s[i >> 2] = (uint8_t)(se + 127);
     }
 }
 
@@ -105,11 +189,15 @@ static unsigned grid_for(int64_t work, int per_block) {
     return (unsigned)(g < 1 ? 1 : g);
 }
 
-hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule,
-                           uint8_t* q, uint8_t* s, hipStream_t stream) {
+hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule, int rounding,
+                           uint64_t seed, uint8_t* q, uint8_t* s, hipStream_t stream) {
     const int64_t nquads = rows * (K / 8);
-    hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3(grid_for(nquads, 256)), dim3(256), 0,
-                       stream, w, q, s, nquads, rule);
+    if (rounding == 1)
+        hipLaunchKernelGGL(mxfp4_quantize_kernel<true>, dim3(grid_for(nquads, 256)), dim3(256), 0,
+                           stream, w, q, s, nquads, rule, seed);
+    else
+        hipLaunchKernelGGL(mxfp4_quantize_kernel<false>, dim3(grid_for(nquads, 256)), dim3(256),
+                           0, stream, w, q, s, nquads, rule, seed);
     return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"mxfp4_quantize", "moe_route", "moe_expert_mlp", "moe_route_workspace_size",
+    assert {"mxfp4_quantize", "mxfp4_quantize_ex", "moe_route", "moe_expert_mlp",
+            "moe_route_workspace_size",
             "moe_expert_mlp_workspace_size", "moe_status_string", "mxfp4_dequantize",
             "moe_abi_version"} <= names
 
@@ -72,7 +73,15 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 def test_quantize_validation(L):
     assert L.mxfp4_quantize(FAKE, 4, 48, 0, FAKE, FAKE, None) == SHAPE
     assert L.mxfp4_quantize(FAKE, -1, 64, 0, FAKE, FAKE, None) == SHAPE
-    assert L.mxfp4_quantize(FAKE, 4, 64, 2, FAKE, FAKE, None) == ENUM
+    assert L.mxfp4_quantize(FAKE, 4, 64, 3, FAKE, FAKE, None) == ENUM
+    L.mxfp4_quantize_ex.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.mxfp4_quantize_ex(FAKE, 4, 64, 2, 2, 0, FAKE, FAKE, None) == ENUM   # rounding
+    assert L.mxfp4_quantize_ex(FAKE, 4, 64, 3, 1, 0, FAKE, FAKE, None) == ENUM   # rule
+    assert L.mxfp4_quantize_ex(FAKE, 4, 48, 2, 1, 0, FAKE, FAKE, None) == SHAPE
+    assert L.mxfp4_quantize_ex(None, 4, 64, 2, 1, 0, FAKE, FAKE, None) == NULL
+    assert L.mxfp4_quantize_ex(None, 0, 64, 2, 1, 0, None, None, None) == OK
     assert L.mxfp4_quantize(None, 4, 64, 0, FAKE, FAKE, None) == NULL
     assert L.mxfp4_quantize(FAKE + 2, 4, 64, 0, FAKE, FAKE, None) == ALIGN
     assert L.mxfp4_quantize(None, 0, 64, 0, None, None, None) == OK    # empty: nothing to do

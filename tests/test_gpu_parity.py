@@ -28,15 +28,15 @@ def log(msg):
     print(msg, flush=True)
 
 
-def gpu_quantize(w_bits, rule=0):
-    q, s = moe.mxfp4_quantize(G.bf16_dev(w_bits), rule)
+def gpu_quantize(w_bits, rule=0, stochastic=False, seed=0):
+    q, s = moe.mxfp4_quantize(G.bf16_dev(w_bits), rule, stochastic=stochastic, seed=seed)
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
 
 # ------------------------------------------------------------------ quantize
 
-@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("rule", [0, 1, 2])
 def test_quantize_every_bf16_as_lone_element(rule):
     w = np.zeros((len(FINITE), 32), np.uint16)
     w[np.arange(len(FINITE)), np.arange(len(FINITE)) % 32] = FINITE
@@ -46,7 +46,7 @@ def test_quantize_every_bf16_as_lone_element(rule):
     assert np.array_equal(q, rq)
 
 
-@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("rule", [0, 1, 2])
 def test_quantize_every_bf16_under_many_maxima(rule):
     rows = []
     for E in (1, 2, 7, 60, 100, 118, 121, 124, 127, 130, 160, 200, 252, 253, 254):
@@ -76,6 +76,57 @@ def test_quantize_random_rows_many_blocks(rule):
     q, s = gpu_quantize(w, rule)
     rq, rs = O.quantize(w, rule)
     assert np.array_equal(s, rs) and np.array_equal(q, rq)
+
+
+# Stochastic rounding: bit-exact against the oracle (same SplitMix64 stream,
+# same threshold), over every finite bf16 value under many block maxima,
+# random rows over 80 binades, the three scale rules and 64-bit seeds.
+def _every_bf16_under_many_maxima():
+    rows = []
+    for E in (1, 2, 7, 60, 100, 118, 121, 124, 127, 130, 160, 200, 252, 253, 254):
+        for M in (0, 63, 64, 65, 127):
+            mx = np.uint16(E << 7 | M)
+            vals = FINITE[(FINITE & 0x7FFF) <= mx]
+            n = (len(vals) + 30) // 31
+            blk = np.zeros((n, 32), np.uint16)
+            flat = np.zeros(n * 31, np.uint16)
+            flat[:len(vals)] = vals
+            blk[:, 1:] = flat.reshape(n, 31)
+            blk[:, 0] = mx | (np.uint16(0x8000) if M == 63 else np.uint16(0))
+            rows.append(blk)
+    return np.concatenate(rows)
+
+
+@pytest.mark.parametrize("rule,seed", [(2, 0), (2, 0xFEDCBA9876543210), (0, 7), (1, 2 ** 63 + 5)])
+def test_quantize_stochastic_every_bf16_under_many_maxima(rule, seed):
+    w = _every_bf16_under_many_maxima()
+    q, s = gpu_quantize(w, rule, stochastic=True, seed=seed)
+    rq, rs = O.quantize(w, rule, stochastic=True, seed=seed)
+    assert np.array_equal(s, rs)
+    assert np.array_equal(q, rq)
+
+
+@pytest.mark.parametrize("rule", [0, 1, 2])
+def test_quantize_stochastic_random_rows(rule):
+    rng = np.random.default_rng(23)
+    v = rng.standard_normal((37, 2880)) * np.exp(rng.uniform(-40, 40, (37, 1)))
+    w = MI.f32_to_bf16_bits(v.astype(np.float32))
+    for seed in (1, 12345):
+        q, s = gpu_quantize(w, rule, stochastic=True, seed=seed)
+        rq, rs = O.quantize(w, rule, stochastic=True, seed=seed)
+        assert np.array_equal(s, rs) and np.array_equal(q, rq), seed
+
+
+def test_quantize_stochastic_seed_determines_the_codes():
+    cfg = MI.CONFIGS["gptoss20b_decode"]
+    w13, _ = MI.gen_expert(cfg, 0, 3)
+    a = gpu_quantize(w13, 2, stochastic=True, seed=99)
+    b = gpu_quantize(w13, 2, stochastic=True, seed=99)
+    c = gpu_quantize(w13, 2, stochastic=True, seed=100)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[1], c[1]) and not np.array_equal(a[0], c[0])
+    rq, rs = O.quantize(w13, 2, stochastic=True, seed=100)
+    assert np.array_equal(c[0], rq) and np.array_equal(c[1], rs)
 
 
 @pytest.mark.parametrize("name", ["tiny", "gptoss20b_decode", "gptoss120b_decode"])
