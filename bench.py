@@ -54,6 +54,13 @@ def algorithmic_work(cfg, counts: np.ndarray) -> dict:
                 step_flops=6 * D * F * pairs, gateup_flops=4 * D * F * pairs)
 
 
+def packed_ok(cfg) -> bool:
+    """Shapes the library accepts with packed weight codes (both expert
+    algorithms: contraction sizes multiples of 64 within the streaming
+    kernels' LDS budget)."""
+    return cfg.D % 64 == 0 and cfg.F % 64 == 0 and cfg.D <= 3840 and cfg.F <= 2944
+
+
 def read_traffic(kernel: str, workload: str, source: str):
     """HBM bytes per dispatch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
@@ -138,6 +145,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algo", default="auto", choices=["auto", "stream", "gemm"],
                     help="expert algorithm (default: the library's automatic choice)")
+    ap.add_argument("--layout", default="auto", choices=["auto", "canonical", "packed"],
+                    help="expert weight code layout (default: packed where the kernels take it)")
     ap.add_argument("--quantize", action="store_true",
                     help="time mxfp4_quantize (nearest-even and stochastic rounding) on the "
                          "workload's W13 instead of the layer")
@@ -176,9 +185,10 @@ def main() -> int:
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
     xd, wrd, bd = bf16(x), torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)
-    base = moe.ExpertWeights.quantize(bf16(w13), bf16(w2))
+    packed = args.layout == "packed" or (args.layout == "auto" and packed_ok(cfg))
+    base = moe.ExpertWeights.quantize(bf16(w13), bf16(w2), packed=packed)
     copies = [base] + [moe.ExpertWeights(base.w13_q.clone(), base.w13_s.clone(),
-                                         base.w2_q.clone(), base.w2_s.clone())
+                                         base.w2_q.clone(), base.w2_s.clone(), packed)
                        for _ in range(NCOPIES - 1)]
     out = torch.empty(cfg.T, cfg.D, dtype=torch.bfloat16, device=dev)
     routing = moe.alloc_routing(cfg.T, cfg.E, cfg.k, dev)
@@ -265,6 +275,7 @@ def main() -> int:
                    "matrix_cores": "block-scaled mfma: mxfp4 weights x fp8 residual terms "
                                    "of the activations, fp32 accumulate",
                    "expert_algorithm": "weight streaming" if decode else "grouped gemm",
+                   "weight_layout": "packed 32x64 fragments" if packed else "row-major",
                    "touched_experts": work["touched"], "weight_copies_rotated": NCOPIES,
                    "parallelism": "single GPU"},
         "roofline": roof,

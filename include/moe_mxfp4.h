@@ -83,8 +83,14 @@ typedef enum {
                                   weight streaming otherwise */
     MOE_MLP_STREAM = 1,        /* weight streaming: each touched expert's weights
                                   are read once per group of 16 of its pairs */
-    MOE_MLP_GROUPED_GEMM = 2   /* tiled grouped GEMM over 128-pair tiles; needs
+    MOE_MLP_GROUPED_GEMM = 2,  /* tiled grouped GEMM over 128-pair tiles; needs
                                   D % 64 == 0 and F % 64 == 0 (else MOE_ERR_SHAPE) */
+    MOE_MLP_WEIGHTS_PACKED = 0x100  /* flag, OR-ed into the algorithm: w13_q and w2_q
+                                  are in the layout mxfp4_pack writes (the scales
+                                  are unchanged); needs D % 64 == 0, F % 64 == 0
+                                  and a shape both algorithms take (the streaming
+                                  kernels' LDS budget: D <= 3840, F <= 2944),
+                                  else MOE_ERR_SHAPE */
 } moe_mlp_algo_t;
 
 /* Human-readable name of a status code (static string). */
@@ -127,6 +133,25 @@ MOE_API moe_status_t mxfp4_quantize(const uint16_t *w, int64_t rows, int64_t K,
 MOE_API moe_status_t mxfp4_quantize_ex(const uint16_t *w, int64_t rows, int64_t K,
                             int scale_rule, int rounding, uint64_t seed,
                             uint8_t *q, uint8_t *s, hipStream_t stream);
+
+/*
+ * mxfp4_pack -- reorder MXFP4 codes for the expert kernels (done once, when
+ * the weights are loaded).
+ *   q    [rows, K/2] codes as mxfp4_quantize writes them
+ *   out  [rows, K/2] bytes: for each 32-row fragment f and 64-element
+ *        contraction step t, the fragment's 32 rows x 32 bytes of that step
+ *        form one contiguous 1 KiB chunk, chunks in (f, t) order; inside a
+ *        chunk the first 32-element half (16 bytes) of rows 0..31 comes
+ *        first, then the second half of rows 0..31:
+ *        out[(f*K/64 + t)*1024 + h*512 + r*16 + b] = q[(32f + r)*K/2 + 32t + 16h + b]
+ *        (h in {0, 1}, r in [0, 32), b in [0, 16))
+ * The expert kernels then read each matrix-core operand fragment (one
+ * 16-byte piece per lane) as one contiguous 1 KiB load instead of 32 row
+ * pieces.  The E8M0 scales keep their layout.  Preconditions: rows % 32 == 0, K % 64 == 0, out does not overlap q.
+ * Errors: MOE_ERR_SHAPE, MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+MOE_API moe_status_t mxfp4_pack(const uint8_t *q, int64_t rows, int64_t K, uint8_t *out,
+                                hipStream_t stream);
 
 /*
  * mxfp4_dequantize -- MXFP4 to bf16 (exact for every scale byte in

@@ -9,9 +9,11 @@ the library is missing, or a tensor is not on the GPU, the call raises.
 Functions mirror the C entry points:
     mxfp4_quantize(w, rule)           -> (q, s)
     mxfp4_dequantize(q, s)            -> bf16 tensor
+    mxfp4_pack(q)                     -> codes reordered for the expert kernels
     moe_route(x, wr, br, k)           -> Routing
     moe_expert_mlp(x, weights, routing, algo=MLP_AUTO) -> bf16 [T, D]
-      (moe_expert_mlp_ex in the C ABI when an algorithm is named)
+      (moe_expert_mlp_ex in the C ABI when an algorithm is named or the
+      weights are packed)
 and MoELayer bundles quantized weights and workspaces for repeated calls.
 """
 
@@ -23,10 +25,11 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["mxfp4_quantize", "mxfp4_dequantize", "moe_route", "moe_expert_mlp",
+__all__ = ["mxfp4_quantize", "mxfp4_dequantize", "mxfp4_pack", "moe_route", "moe_expert_mlp",
            "Routing", "ExpertWeights", "MoELayer", "MoEError", "lib",
            "SCALE_FLOOR_DIV6", "SCALE_OCP", "SCALE_CEIL_DIV6", "ROUND_NEAREST_EVEN",
-           "ROUND_STOCHASTIC", "MLP_AUTO", "MLP_STREAM", "MLP_GROUPED_GEMM", "LIB_PATH"]
+           "ROUND_STOCHASTIC", "MLP_AUTO", "MLP_STREAM", "MLP_GROUPED_GEMM", "MLP_WEIGHTS_PACKED",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
 SCALE_FLOOR_DIV6 = 0
@@ -34,6 +37,7 @@ SCALE_OCP = 1
 SCALE_CEIL_DIV6 = 2
 ROUND_NEAREST_EVEN, ROUND_STOCHASTIC = 0, 1
 MLP_AUTO, MLP_STREAM, MLP_GROUPED_GEMM = 0, 1, 2
+MLP_WEIGHTS_PACKED = 0x100   # flag OR-ed into the algorithm: codes in mxfp4_pack's layout
 
 
 class MoEError(RuntimeError):
@@ -67,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.mxfp4_quantize_ex.restype = ctypes.c_int
         L.mxfp4_dequantize.argtypes = [P, P, i64, i64, P, P]
         L.mxfp4_dequantize.restype = ctypes.c_int
+        L.mxfp4_pack.argtypes = [P, i64, i64, P, P]
+        L.mxfp4_pack.restype = ctypes.c_int
         L.moe_route_workspace_size.argtypes = [i32, i32, i32, i32]
         L.moe_route_workspace_size.restype = sz
         L.moe_route.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
@@ -129,6 +135,19 @@ def mxfp4_dequantize(q: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def mxfp4_pack(q: torch.Tensor) -> torch.Tensor:
+    """Codes uint8 [..., K/2] (rows a multiple of 32, K % 64 == 0) -> the same
+    codes with each 32-row x 64-element fragment contiguous (1 KiB: the first
+    32-element halves of its 32 rows, then the second halves), fragments in
+    (row group, contraction step) order.  The scales keep their layout."""
+    K = q.shape[-1] * 2
+    rows = q.numel() // q.shape[-1] if q.shape[-1] else 0
+    out = torch.empty_like(q)
+    _check("mxfp4_pack", lib().mxfp4_pack(_dev(q, "q", torch.uint8), rows, K, _dev(out, "out"),
+                                          _stream(q.device)))
+    return out
+
+
 # ---------------------------------------------------------------- routing
 
 @dataclass
@@ -185,6 +204,7 @@ class ExpertWeights:
     w13_s: torch.Tensor   # uint8 [E, 2F, D/32]
     w2_q: torch.Tensor    # uint8 [E, D, F/2]
     w2_s: torch.Tensor    # uint8 [E, D, F/32]
+    packed: bool = False  # codes (w13_q, w2_q) in mxfp4_pack's layout
 
     @property
     def E(self) -> int:
@@ -198,12 +218,25 @@ class ExpertWeights:
     def D(self) -> int:
         return self.w2_q.shape[1]
 
+    @property
+    def algo_flags(self) -> int:
+        return MLP_WEIGHTS_PACKED if self.packed else 0
+
+    def pack(self) -> "ExpertWeights":
+        """The same weights with the codes in mxfp4_pack's layout."""
+        if self.packed:
+            return self
+        return ExpertWeights(mxfp4_pack(self.w13_q), self.w13_s, mxfp4_pack(self.w2_q),
+                             self.w2_s, True)
+
     @classmethod
-    def quantize(cls, w13: torch.Tensor, w2: torch.Tensor, rule: int = SCALE_FLOOR_DIV6):
-        """bf16 W13 [E, 2F, D] and W2 [E, D, F] -> MXFP4."""
+    def quantize(cls, w13: torch.Tensor, w2: torch.Tensor, rule: int = SCALE_FLOOR_DIV6,
+                 packed: bool = False):
+        """bf16 W13 [E, 2F, D] and W2 [E, D, F] -> MXFP4 (codes packed on request)."""
         a, b = mxfp4_quantize(w13, rule)
         c, d = mxfp4_quantize(w2, rule)
-        return cls(a, b, c, d)
+        w = cls(a, b, c, d)
+        return w.pack() if packed else w
 
 
 def _event_array(events) -> ctypes.Array:
@@ -242,8 +275,8 @@ def moe_expert_mlp(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
         _dev(routing.offsets, "offsets", torch.int32),
         _dev(routing.sorted_pairs, "sorted_pairs", torch.int32),
         _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
-        _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), algo, ev,
-        _stream(x.device)))
+        _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), algo | weights.algo_flags,
+        ev, _stream(x.device)))
     return out
 
 
@@ -298,7 +331,7 @@ class PreparedLayer:
             _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w"),
             _dev(routing.offsets, "offsets"), _dev(routing.sorted_pairs, "sorted_pairs"),
             _dev(routing.pair_pos, "pair_pos"), T, D, F, E, k, _dev(out, "out", torch.bfloat16),
-            _dev(mlp_ws, "ws"), mlp_ws.numel(), algo)
+            _dev(mlp_ws, "ws"), mlp_ws.numel(), algo | weights.algo_flags)
         self.stream = st
 
     @staticmethod

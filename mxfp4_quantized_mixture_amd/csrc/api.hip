@@ -64,6 +64,18 @@ moe_status_t mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, 
     return hip_status(moe::launch_dequantize(q, s, rows, K, out, stream));
 }
 
+moe_status_t mxfp4_pack(const uint8_t* q, int64_t rows, int64_t K, uint8_t* out,
+                        hipStream_t stream) {
+    if (rows < 0 || K <= 0 || K % 64 != 0 || rows % 32 != 0) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!q || !out) return MOE_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return MOE_ERR_ALIGN;
+    const uintptr_t a0 = (uintptr_t)q, a1 = a0 + (uintptr_t)(rows * (K / 2));
+    const uintptr_t b0 = (uintptr_t)out, b1 = b0 + (uintptr_t)(rows * (K / 2));
+    if (a0 < b1 && b0 < a1) return MOE_ERR_SHAPE;       // in place or overlapping
+    return hip_status(moe::launch_pack(q, rows, K, out, stream));
+}
+
 size_t moe_route_workspace_size(int32_t T, int32_t D, int32_t E, int32_t k) {
     if (!route_shape_ok(T, D, E, k)) return 0;
     return moe::plan_route(T, D, E, k).ws_bytes;
@@ -106,20 +118,24 @@ moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const ui
                                const int32_t* pair_pos, int32_t T, int32_t D, int32_t F,
                                int32_t E, int32_t k, uint16_t* out, void* ws, size_t ws_bytes,
                                int algo, hipEvent_t* stage_events, hipStream_t stream) {
-    if (algo != MOE_MLP_AUTO && algo != MOE_MLP_STREAM && algo != MOE_MLP_GROUPED_GEMM)
+    const bool packed = (algo & MOE_MLP_WEIGHTS_PACKED) != 0;
+    const int base = algo & ~MOE_MLP_WEIGHTS_PACKED;
+    if (base != MOE_MLP_AUTO && base != MOE_MLP_STREAM && base != MOE_MLP_GROUPED_GEMM)
         return MOE_ERR_ENUM;
     if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return MOE_ERR_SHAPE;
-    if (algo == MOE_MLP_GROUPED_GEMM && (D % 64 != 0 || F % 64 != 0)) return MOE_ERR_SHAPE;
+    if (base == MOE_MLP_GROUPED_GEMM && (D % 64 != 0 || F % 64 != 0)) return MOE_ERR_SHAPE;
     if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !offsets || !sorted_pairs ||
         !pair_pos || !out)
         return MOE_ERR_NULL;
     const moe::MlpPlan plan = moe::plan_mlp(T, D, F, E, k);
+    if (packed && !plan.packed_ok) return MOE_ERR_SHAPE;
     if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
         !aligned16(w2_s) || !aligned16(out) || !aligned16(ws))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_mlp(plan, algo, x, w13_q, w13_s, w2_q, w2_s, topk_w, offsets,
-                                      sorted_pairs, pair_pos, out, ws, stage_events, stream));
+    return hip_status(moe::launch_mlp(plan, base, packed, x, w13_q, w13_s, w2_q, w2_s, topk_w,
+                                      offsets, sorted_pairs, pair_pos, out, ws, stage_events,
+                                      stream));
 }
 
 }  // extern "C"

@@ -172,7 +172,11 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 // buffers, weights global -> registers, each a stage ahead, with one
 // barrier per stage.
 // ---------------------------------------------------------------------------
-template <bool kGateUp, int kStage, int WR, int WP>
+// kPacked: wq in the mxfp4_pack layout (a fragment's 32 rows x 32 bytes of
+// one step are a contiguous 1 KiB chunk: 16-byte piece 32 h + r holds half h
+// of row r), so lane (n, g)'s A piece of step st is the 16 bytes at
+// 16 lane + 1024 st from the fragment's first chunk.
+template <bool kGateUp, int kStage, int WR, int WP, bool kPacked>
 __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kernel(
     const uint8_t* __restrict__ bq, const int32_t* __restrict__ sorted, int k,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
@@ -241,7 +245,9 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
         const int slot = kGateUp ? (a & 1) : a;         // gate/up: a = 0, 1 gate; 2, 3 up
         const int f = slot < wcnt ? wf0 + slot : fa;    // idle fragments recompute fragment fa
         const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
-        aoff[a] = (uint32_t)(((size_t)e * R + frow + n) * (size_t)(K / 2) + 16 * g);
+        // (the fragment's first byte is the same in both layouts)
+        aoff[a] = kPacked ? (uint32_t)(((size_t)e * R + frow) * (size_t)(K / 2) + 16 * lane)
+                          : (uint32_t)(((size_t)e * R + frow + n) * (size_t)(K / 2) + 16 * g);
     }
     // Direct global -> LDS loads (lane l writes 16 bytes at the wave-uniform
     // destination + 16 l), all issued before the prologue barrier, so the
@@ -307,7 +313,8 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
             }
 #pragma unroll
             for (int a = 0; a < NA; ++a)
-                a_nxt[kk][a] = *reinterpret_cast<const u32x4_t*>(wq + (aoff[a] + 32u * st));
+                a_nxt[kk][a] = *reinterpret_cast<const u32x4_t*>(
+                    wq + (aoff[a] + (kPacked ? 1024u : 32u) * st));
         }
     };
     auto advance_a = [&]() {
@@ -510,7 +517,7 @@ size_t gemm_lds_bytes(int K, int NT, int stage, int wr) {
 }
 
 
-template <bool kGateUp, int kStage, int WR, int WP>
+template <bool kGateUp, int kStage, int WR, int WP, bool kPacked>
 static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t* sorted,
                               const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
                               int K, int NOUT, uint8_t* hq, float* y, hipStream_t stream) {
@@ -520,11 +527,11 @@ static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t
         lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * term_chunk(3));
     if (lds > 65536) {
         const hipError_t er = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage, WR, WP>),
+            reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage, WR, WP, kPacked>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (er != hipSuccess) return er;
     }
-    hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, kStage, WR, WP>),
+    hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, kStage, WR, WP, kPacked>),
                        dim3((unsigned)gemm_grid(p.max_tiles, ntl)), dim3(64 * WR * WP), lds,
                        stream, bq, sorted, p.k, wq, ws, tiles, p.max_tiles, ntl, K, NOUT, p.F,
                        hq, y);
@@ -532,7 +539,7 @@ static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t
 }
 
 
-hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                            const int32_t* offsets, const int32_t* sorted, float* y, char* base,
                            hipEvent_t* events, hipStream_t stream) {
@@ -549,13 +556,19 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w
         if (er != hipSuccess) return er;
     }
     hipError_t er;
-    er = launch_gemm<true, 1, 2, 2>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq, nullptr, stream);
+    er = packed ? launch_gemm<true, 1, 2, 2, true>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq,
+                                                   nullptr, stream)
+                : launch_gemm<true, 1, 2, 2, false>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq,
+                                                    nullptr, stream);
     if (er != hipSuccess) return er;
     if (events) {
         er = hipEventRecord(events[1], stream);
         if (er != hipSuccess) return er;
     }
-    er = launch_gemm<false, 1, 4, 2>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D, nullptr, y, stream);
+    er = packed ? launch_gemm<false, 1, 4, 2, true>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D,
+                                                    nullptr, y, stream)
+                : launch_gemm<false, 1, 4, 2, false>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D,
+                                                     nullptr, y, stream);
     if (er != hipSuccess) return er;
     return hipGetLastError();
 }

@@ -364,18 +364,31 @@ struct WBatch {
     u32x4_t q[NB];
 };
 
-// Load NB super-steps (from ss0) of one 16-row weight tile (this lane's row
-// q); out-of-range blocks are clamped to the row's last block (finite data,
-// multiplied by zero activations).
-template <int NB>
+// Load NB super-steps (from ss0) of one 16-row weight tile (q: this lane's
+// row, see row_base); out-of-range blocks are clamped to the row's last block
+// (finite data, multiplied by zero activations).  Block blk of the row is at
+// 16 blk, or with packed codes (mxfp4_pack: 32-row fragments, 1 KiB per
+// 64-element step, its two 32-element halves 512 bytes apart) at
+// 1024 (blk / 2) + 512 (blk % 2) from the row's first piece.
+template <int NB, bool kPacked>
 __device__ __forceinline__ void load_batch(WBatch<NB>& B, const uint8_t* q, int ss0, int g,
                                            int nblk) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         int blk = (ss0 + i) * 4 + g;
         blk = blk < nblk ? blk : nblk - 1;
-        B.q[i] = *reinterpret_cast<const u32x4_t*>(q + blk * 16);
+        const int off = kPacked ? (blk >> 1) * 1024 + (blk & 1) * 512 : blk * 16;
+        B.q[i] = *reinterpret_cast<const u32x4_t*>(q + off);
     }
+}
+
+// Where weight row `row` (of a matrix with rowbytes bytes per row) starts for
+// load_batch: the row itself, or with packed codes its first 16-byte piece in
+// the first chunk of its 32-row fragment (a fragment's first byte is the same
+// in both layouts).
+template <bool kPacked>
+__device__ __forceinline__ const uint8_t* row_base(const uint8_t* q, size_t row, size_t rowbytes) {
+    return kPacked ? q + (row & ~(size_t)31) * rowbytes + (row & 31) * 16 : q + row * rowbytes;
 }
 
 // The E8M0 scales of a 16-row weight tile are one contiguous 16 * nblk-byte
@@ -460,7 +473,7 @@ __device__ __forceinline__ void compute_batch(const WBatch<NB>& B, int ss0, int 
 // weight stream instead of queueing behind it.  The expert's pairs are taken
 // 16 at a time (one pass over the tiles per group of 16; decode steps have
 // one group); blocks of experts without pairs exit before loading anything.
-template <bool kGateUp>
+template <bool kGateUp, bool kPacked>
 __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ offsets,
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     auto row_of = [&](int s) {
         const int tile = tile_at(s / seg);
         const int r = NS == 1 ? 0 : (s / nbt) % NS;   // up rows follow the F gate rows
-        return qe + (size_t)(r * F + tile * 16 + m) * rowbytes;
+        return row_base<kPacked>(qe, (size_t)(r * F + tile * 16 + m), rowbytes);
     };
     auto runs_of = [&](int tile, const uint8_t* (&run)[NS]) {
 #pragma unroll
@@ -511,7 +524,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
     const int last = steps > 0 ? steps - 1 : 0;
     auto fetch = [&](WBatch<NB>& W, int s) {
         const int sc_ = s < last ? s : last;
-        load_batch<NB>(W, row_of(sc_), (sc_ % nbt) * NB, g, nblk);
+        load_batch<NB, kPacked>(W, row_of(sc_), (sc_ % nbt) * NB, g, nblk);
     };
     WBatch<NB> B0, B1, B2;
     ScaleRegs<NS> SR;
@@ -634,6 +647,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+constexpr size_t kMaxStreamLds = 158 * 1024;   // of 160 KiB, leaving room for static LDS
+
+// Staged fp8 terms of 16 rows of K elements: ceil(K/128) super-steps x NT
+// terms x 64 lanes x (32 data bytes + 1 scale byte).
+static size_t stream_lds_bytes(int K, int NT, int NS) {
+    return (size_t)((K / 32 + 3) / 4) * NT * 64 * 33 + (size_t)kStreamWaves * NS * 16 * (K / 32);
+}
+
 MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     MlpPlan p{};
     p.T = T; p.D = D; p.F = F; p.E = E; p.k = k;
@@ -648,6 +669,9 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     // pairs; the grouped GEMM stages 128-pair tiles.  Switch once the average
     // expert receives 32 pairs.
     p.gemm_auto = p.gemm_ok && P >= (size_t)32 * E;
+    p.stream_ok = stream_lds_bytes(D, 2, 2) <= kMaxStreamLds &&
+                  stream_lds_bytes(F, 3, 1) <= kMaxStreamLds && D <= 4096 && F <= 4096;
+    p.packed_ok = p.gemm_ok && p.stream_ok;
     p.max_tiles = gemm_max_tiles(T, E, k);
     p.off_y = 0;
     const size_t scratch = align256(P * D * sizeof(float));
@@ -662,14 +686,6 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     }
     p.ws_bytes = std::max(stream_end, gemm_end);
     return p;
-}
-
-constexpr size_t kMaxStreamLds = 158 * 1024;   // of 160 KiB, leaving room for static LDS
-
-// Staged fp8 terms of 16 rows of K elements: ceil(K/128) super-steps x NT
-// terms x 64 lanes x (32 data bytes + 1 scale byte).
-static size_t stream_lds_bytes(int K, int NT, int NS) {
-    return (size_t)((K / 32 + 3) / 4) * NT * 64 * 33 + (size_t)kStreamWaves * NS * 16 * (K / 32);
 }
 
 // Blocks per expert for the streaming kernels: about 256 blocks in all (one
@@ -695,18 +711,39 @@ static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* 
                                  const int32_t* pos, uint16_t* out, hipEvent_t* events,
                                  hipStream_t stream);
 
-hipError_t launch_mlp(const MlpPlan& p, int algo, const uint16_t* x, const uint8_t* w13q,
-                      const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                      const float* topk_w, const int32_t* offsets, const int32_t* sorted,
-                      const int32_t* pos, uint16_t* out, void* ws, hipEvent_t* events,
-                      hipStream_t stream) {
+// One streaming pass: gate/up (kGateUp, K = D, F output rows per expert) or
+// down (K = F, D output rows), blocks sized by stream_blocks_per_expert.
+template <bool kGateUp, bool kPacked>
+static hipError_t launch_stream(const MlpPlan& p, const void* act, const uint8_t* wq,
+                                const uint8_t* ws_, const int32_t* offsets,
+                                const int32_t* sorted, void* out, hipStream_t stream) {
+    const size_t lds = kGateUp ? stream_lds_bytes(p.D, 2, 2) : stream_lds_bytes(p.F, 3, 1);
+    const int bpe = stream_blocks_per_expert(p.E, (kGateUp ? p.F : p.D) / 16);
+    if (lds > 65536) {
+        const hipError_t er =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<kGateUp, kPacked>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (er != hipSuccess) return er;
+    }
+    hipLaunchKernelGGL((expert_stream_kernel<kGateUp, kPacked>), dim3(p.E * bpe),
+                       dim3(kStreamWaves * 64), lds, stream,
+                       reinterpret_cast<const uint16_t*>(act), wq, ws_, offsets, sorted, p.D,
+                       p.F, p.E, p.k, bpe, out);
+    return hipSuccess;
+}
+
+hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x,
+                      const uint8_t* w13q, const uint8_t* w13s, const uint8_t* w2q,
+                      const uint8_t* w2s, const float* topk_w, const int32_t* offsets,
+                      const int32_t* sorted, const int32_t* pos, uint16_t* out, void* ws,
+                      hipEvent_t* events, hipStream_t stream) {
     char* base = static_cast<char*>(ws);
     _Float16* h = reinterpret_cast<_Float16*>(base + p.off_h);
     float* y = reinterpret_cast<float*>(base + p.off_y);
     const bool gemm = algo == 2 || (algo == 0 && p.gemm_auto);
     if (gemm) {
-        const hipError_t er = launch_mlp_gemm(p, x, w13q, w13s, w2q, w2s, offsets, sorted, y,
-                                              base, events, stream);
+        const hipError_t er = launch_mlp_gemm(p, packed, x, w13q, w13s, w2q, w2s, offsets, sorted,
+                                              y, base, events, stream);
         if (er != hipSuccess) return er;
         return launch_combine(p, y, topk_w, pos, out, events, stream);
     }
@@ -714,32 +751,18 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, const uint16_t* x, const uint8
         const hipError_t er = hipEventRecord(events[0], stream);
         if (er != hipSuccess) return er;
     }
-    const size_t lds_gu = stream_lds_bytes(p.D, 2, 2), lds_dn = stream_lds_bytes(p.F, 3, 1);
-    if (lds_gu <= kMaxStreamLds && lds_dn <= kMaxStreamLds && p.D <= 4096 && p.F <= 4096) {
-        const int bpe1 = stream_blocks_per_expert(p.E, p.F / 16);
-        const int g1 = p.E * bpe1;
-        if (lds_gu > 65536) {
-            hipError_t er = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<true>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu);
-            if (er != hipSuccess) return er;
-        }
-        hipLaunchKernelGGL(expert_stream_kernel<true>, dim3(g1), dim3(kStreamWaves * 64), lds_gu,
-                           stream, x, w13q, w13s, offsets, sorted, p.D, p.F, p.E, p.k, bpe1,
-                           static_cast<void*>(h));
+    if (p.stream_ok) {
+        hipError_t er = packed
+            ? launch_stream<true, true>(p, x, w13q, w13s, offsets, sorted, h, stream)
+            : launch_stream<true, false>(p, x, w13q, w13s, offsets, sorted, h, stream);
+        if (er != hipSuccess) return er;
         if (events) {
-            const hipError_t er = hipEventRecord(events[1], stream);
+            er = hipEventRecord(events[1], stream);
             if (er != hipSuccess) return er;
         }
-        const int bpe2 = stream_blocks_per_expert(p.E, p.D / 16);
-        const int g2 = p.E * bpe2;
-        if (lds_dn > 65536) {
-            hipError_t er = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_stream_kernel<false>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn);
-            if (er != hipSuccess) return er;
-        }
-        hipLaunchKernelGGL(expert_stream_kernel<false>, dim3(g2), dim3(kStreamWaves * 64), lds_dn,
-                           stream, reinterpret_cast<const uint16_t*>(h), w2q, w2s, offsets, sorted,
-                           p.D, p.F, p.E, p.k, bpe2, static_cast<void*>(y));
+        er = packed ? launch_stream<false, true>(p, h, w2q, w2s, offsets, sorted, y, stream)
+                    : launch_stream<false, false>(p, h, w2q, w2s, offsets, sorted, y, stream);
+        if (er != hipSuccess) return er;
     } else {
         const int bpe1 = blocks_per_expert(p.E, p.F / 16);
         hipLaunchKernelGGL(gateup_stream_kernel, dim3(p.E * bpe1), dim3(256), 0, stream, x, w13q,

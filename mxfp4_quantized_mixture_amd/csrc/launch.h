@@ -11,6 +11,8 @@ hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule,
                            uint64_t seed, uint8_t* q, uint8_t* s, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
                              uint16_t* out, hipStream_t stream);
+hipError_t launch_pack(const uint8_t* q, int64_t rows, int64_t K, uint8_t* out,
+                       hipStream_t stream);
 
 struct RoutePlan {
     int T, D, E, k;
@@ -31,6 +33,8 @@ struct MlpPlan {
     int T, D, F, E, k;
     bool gemm_ok;        // grouped-GEMM path possible: D % 64 == 0 and F % 64 == 0
     bool gemm_auto;      // grouped-GEMM path chosen when the caller leaves it open
+    bool stream_ok;      // the streaming kernels take the shape (their LDS budget)
+    bool packed_ok;      // packed weights accepted: both algorithms take the shape
     int max_tiles;       // upper bound of 128-pair tiles over all experts
     size_t off_y;
     size_t off_h;                                    // streaming: h fp16 [P, F]
@@ -38,8 +42,9 @@ struct MlpPlan {
     size_t ws_bytes;
 };
 MlpPlan plan_mlp(int T, int D, int F, int E, int k);
-// algo: 0 = automatic, 1 = weight streaming, 2 = grouped GEMM (requires gemm_ok)
-hipError_t launch_mlp(const MlpPlan& p, int algo, const uint16_t* x, const uint8_t* w13q,
+// algo: 0 = automatic, 1 = weight streaming, 2 = grouped GEMM (requires gemm_ok);
+// packed: w13q and w2q in the mxfp4_pack layout (requires packed_ok)
+hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x, const uint8_t* w13q,
                       const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                       const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                       const int32_t* pos, uint16_t* out, void* ws, hipEvent_t* events,
@@ -51,7 +56,7 @@ size_t gemm_term_bytes(int rows, int K, int NT);
 size_t gemm_lds_bytes(int K, int NT, int stage, int wr);
 constexpr size_t kGemmMaxLds = 159 * 1024;    // of 160 KiB; the rest is static LDS
 constexpr int kGemmMaxContraction = 8192;      // D and F limit of the grouped GEMM
-hipError_t launch_mlp_gemm(const MlpPlan& p, const uint16_t* x, const uint8_t* w13q,
+hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                            const int32_t* offsets, const int32_t* sorted, float* y, char* base,
                            hipEvent_t* events, hipStream_t stream);

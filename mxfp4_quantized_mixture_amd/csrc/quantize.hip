@@ -183,6 +183,25 @@ __global__ __launch_bounds__(256) void mxfp4_dequantize_kernel(
     }
 }
 
+// Packed code layout for the expert kernels: for each 32-row fragment f and
+// each 64-element contraction step t, the fragment's 32 rows x 32 bytes of
+// that step are one contiguous 1 KiB chunk, chunks in (f, t) order:
+//   packed[(f * K/64 + t) * 1024 + r * 32 + j] = q[(32 f + r) * K/2 + 32 t + j].
+// One thread per 16 bytes of output (coalesced writes, 32-byte gathers).
+__global__ __launch_bounds__(256) void mxfp4_pack_kernel(const uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ out,
+                                                         int64_t n16, int64_t K) {
+    const int64_t steps = K / 64;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n16; o += stride) {
+        const int64_t chunk = o >> 6;              // 1 KiB chunk (f, t)
+        const int piece = (int)(o & 63);           // 16-byte piece: half h = piece / 32, row r
+        const int64_t f = chunk / steps, t = chunk - f * steps;
+        const int64_t src = (32 * f + (piece & 31)) * (K / 2) + 32 * t + 16 * (piece >> 5);
+        *reinterpret_cast<u32x4_t*>(out + o * 16) = *reinterpret_cast<const u32x4_t*>(q + src);
+    }
+}
+
 static unsigned grid_for(int64_t work, int per_block) {
     int64_t g = (work + per_block - 1) / per_block;
     if (g > 16384) g = 16384;
@@ -198,6 +217,14 @@ hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, int rule,
     else
         hipLaunchKernelGGL(mxfp4_quantize_kernel<false>, dim3(grid_for(nquads, 256)), dim3(256),
                            0, stream, w, q, s, nquads, rule, seed);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* q, int64_t rows, int64_t K, uint8_t* out,
+                       hipStream_t stream) {
+    const int64_t n16 = rows * (K / 2) / 16;
+    hipLaunchKernelGGL(mxfp4_pack_kernel, dim3(grid_for(n16, 256)), dim3(256), 0, stream, q, out,
+                       n16, K);
     return hipGetLastError();
 }
 

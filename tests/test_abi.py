@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"mxfp4_quantize", "mxfp4_quantize_ex", "moe_route", "moe_expert_mlp",
+    assert {"mxfp4_quantize", "mxfp4_quantize_ex", "mxfp4_pack", "moe_route", "moe_expert_mlp",
             "moe_route_workspace_size",
             "moe_expert_mlp_workspace_size", "moe_status_string", "mxfp4_dequantize",
             "moe_abi_version"} <= names
@@ -89,6 +89,17 @@ def test_quantize_validation(L):
     assert L.mxfp4_dequantize(FAKE, None, 4, 64, FAKE, None) == NULL
 
 
+def test_pack_validation(L):
+    assert L.mxfp4_pack(FAKE, 48, 64, FAKE + 4096, None) == SHAPE        # rows % 32
+    assert L.mxfp4_pack(FAKE, 32, 96, FAKE + 4096, None) == SHAPE        # K % 64
+    assert L.mxfp4_pack(FAKE, -32, 64, FAKE + 4096, None) == SHAPE
+    assert L.mxfp4_pack(None, 32, 64, FAKE, None) == NULL
+    assert L.mxfp4_pack(FAKE + 8, 32, 64, FAKE + 4096, None) == ALIGN
+    assert L.mxfp4_pack(FAKE, 32, 64, FAKE, None) == SHAPE               # in place
+    assert L.mxfp4_pack(FAKE, 32, 64, FAKE + 512, None) == SHAPE         # overlapping
+    assert L.mxfp4_pack(None, 0, 64, None, None) == OK
+
+
 def _route(L, T=8, D=64, E=4, k=2, x=FAKE, ws=FAKE, ws_bytes=None, null_out=False):
     if ws_bytes is None:
         ws_bytes = L.moe_route_workspace_size(T, D, E, k) or 1 << 20
@@ -137,6 +148,13 @@ def test_mlp_algorithm_validation(L):
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=160) == SHAPE     # ... and F % 64
     assert _mlp_ex(L, moe.MLP_STREAM, out=None) == NULL
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, out=None) == NULL
+    P = moe.MLP_WEIGHTS_PACKED
+    assert _mlp_ex(L, 0x200) == ENUM                                    # unknown flag
+    assert _mlp_ex(L, 3 | P) == ENUM
+    assert _mlp_ex(L, moe.MLP_STREAM | P, F=160) == SHAPE               # packed needs F % 64
+    assert _mlp_ex(L, moe.MLP_AUTO | P, D=96) == SHAPE                  # ... and D % 64
+    assert _mlp_ex(L, moe.MLP_STREAM | P, D=3904) == SHAPE              # streaming LDS budget
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM | P, F=3008) == SHAPE
 
 
 def test_mlp_workspace_covers_both_algorithms(L):

@@ -267,12 +267,19 @@ class Inputs:
         self.w13, self.w2 = MI.gen_experts(cfg, seed, threads=G.THREADS)
 
 
-def run_gpu_layer(inp, algo=moe.MLP_AUTO):
+def packed_ok(cfg):
+    """Shapes whose expert weights the library takes in the packed layout."""
+    return cfg.D % 64 == 0 and cfg.F % 64 == 0 and cfg.D <= 3840 and cfg.F <= 2944
+
+
+def run_gpu_layer(inp, algo=moe.MLP_AUTO, packed=False):
+    """Route and run the experts; returns the weights in row-major layout (for
+    comparison with the oracle's codes) whichever layout the kernels read."""
     cfg = inp.cfg
     xd = G.bf16_dev(inp.x)
     weights = moe.ExpertWeights.quantize(G.bf16_dev(inp.w13), G.bf16_dev(inp.w2))
     r = moe.moe_route(xd, G.f32_dev(inp.wr), G.f32_dev(inp.b), cfg.k)
-    out = moe.moe_expert_mlp(xd, weights, r, algo=algo)
+    out = moe.moe_expert_mlp(xd, weights.pack() if packed else weights, r, algo=algo)
     torch.cuda.synchronize()
     return weights, r, out
 
@@ -290,9 +297,9 @@ def sample_tokens(ids, T, rng, n_random=12):
     return np.array(sorted(toks))
 
 
-def check_layer(inp, tokens="all", what="", algo=moe.MLP_AUTO):
+def check_layer(inp, tokens="all", what="", algo=moe.MLP_AUTO, packed=False):
     cfg = inp.cfg
-    weights, r, out = run_gpu_layer(inp, algo)
+    weights, r, out = run_gpu_layer(inp, algo, packed)
     ref_r = O.route(inp.x, inp.wr, inp.b, cfg.k)
     ok_tok = np.nonzero(ref_r["gap"] >= NEAR_TIE)[0]
     gids = r.ids.cpu().numpy()
@@ -333,7 +340,9 @@ def test_layer_tiny(seed):
                                          ("gptoss20b_prefill", "sample"),
                                          ("gptoss120b_prefill_skewed", "sample")])
 def test_layer_workloads(name, tokens):
-    check_layer(Inputs(MI.CONFIGS[name], 0), tokens=tokens, what=name)
+    # in the weight layout the benchmark uses: packed wherever the kernels take it
+    cfg = MI.CONFIGS[name]
+    check_layer(Inputs(cfg, 0), tokens=tokens, what=name, packed=packed_ok(cfg))
 
 
 EDGE = [
@@ -409,3 +418,83 @@ def test_moe_layer_object_matches_calls():
     out2 = layer(G.bf16_dev(inp.x))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ------------------------------------------------------------ packed weights
+
+def pack_reference(q):
+    """mxfp4_pack's layout written with numpy: bytes [32t + 16h, 32t + 16h + 16)
+    of row r of 32-row fragment f go to chunk (f, t), byte 512h + 16r of it."""
+    rows, half = q.shape
+    return np.ascontiguousarray(
+        q.reshape(rows // 32, 32, half // 32, 2, 16).transpose(0, 2, 3, 1, 4)).reshape(rows, half)
+
+
+@pytest.mark.parametrize("rows,K", [(32, 64), (96, 192), (64, 2880), (2 * 2880, 2880),
+                                    (32 * 40, 4096)])
+def test_pack_matches_reorder(rows, K):
+    log("pack rows=%d K=%d" % (rows, K))
+    q = np.random.default_rng(rows + K).integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    got = moe.mxfp4_pack(torch.from_numpy(q).cuda()).cpu().numpy()
+    assert np.array_equal(got, pack_reference(q))
+
+
+def test_pack_of_expert_stack_is_per_expert():
+    # [E, R, K/2] packs as E*R rows; with R % 32 == 0 no fragment spans experts
+    q = np.random.default_rng(1).integers(0, 256, (4, 96, 64), dtype=np.uint8)
+    got = moe.mxfp4_pack(torch.from_numpy(q).cuda()).cpu().numpy()
+    for e in range(4):
+        assert np.array_equal(got[e], pack_reference(q[e]))
+
+
+def test_pack_errors():
+    with pytest.raises(moe.MoEError):
+        moe.mxfp4_pack(torch.zeros(48, 32, dtype=torch.uint8, device="cuda"))    # rows % 32
+    with pytest.raises(moe.MoEError):
+        moe.mxfp4_pack(torch.zeros(32, 48, dtype=torch.uint8, device="cuda"))    # K % 64
+    empty = moe.mxfp4_pack(torch.zeros(0, 32, dtype=torch.uint8, device="cuda"))
+    assert empty.shape == (0, 32)
+
+
+# The packed layout changes where the kernels load the codes, not what they
+# compute: the layer output is bit-identical to the row-major run.
+PACKED_CASES = [
+    ("tiny", None), ("gptoss20b_decode", None), ("gemm_ragged", None),
+    ("gemm_full_width", None), ("gemm_outliers", None),
+    ("stream_max_lds", MI.MoEConfig("stream_max_lds", T=9, D=3840, F=2944, E=2, k=1)),
+    ("sparse_experts", MI.MoEConfig("sparse_experts", T=5, D=128, F=192, E=64, k=3)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", PACKED_CASES, ids=[c[0] for c in PACKED_CASES])
+@pytest.mark.parametrize("algo", [moe.MLP_STREAM, moe.MLP_GROUPED_GEMM])
+def test_packed_weights_bit_identical(name, cfg, algo):
+    if cfg is None:
+        cfg = MI.CONFIGS.get(name) or {c.name: c for c in GEMM_EDGE}[name]
+    log("packed %s algo=%d" % (name, algo))
+    inp = Inputs(cfg, 6)
+    xd = G.bf16_dev(inp.x)
+    w = moe.ExpertWeights.quantize(G.bf16_dev(inp.w13), G.bf16_dev(inp.w2))
+    wp = w.pack()
+    r = moe.moe_route(xd, G.f32_dev(inp.wr), G.f32_dev(inp.b), cfg.k)
+    a = moe.moe_expert_mlp(xd, w, r, algo=algo)
+    b = moe.moe_expert_mlp(xd, wp, r, algo=algo)
+    torch.cuda.synchronize()
+    assert torch.equal(wp.w13_s, w.w13_s) and torch.equal(wp.w2_s, w.w2_s)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+
+
+def test_packed_weights_against_oracle_full_width_gemm():
+    cfg = {c.name: c for c in GEMM_EDGE}["gemm_full_width"]
+    check_layer(Inputs(cfg, 8), tokens="sample", what="gemm_full_width/packed",
+                algo=moe.MLP_GROUPED_GEMM, packed=True)
+
+
+def test_packed_weights_rejected_where_the_kernels_cannot_take_them():
+    cfg = MI.MoEConfig("too_wide", T=4, D=3904, F=64, E=2, k=1)
+    inp = Inputs(cfg, 1)
+    xd = G.bf16_dev(inp.x)
+    w = moe.ExpertWeights.quantize(G.bf16_dev(inp.w13), G.bf16_dev(inp.w2)).pack()
+    r = moe.moe_route(xd, G.f32_dev(inp.wr), G.f32_dev(inp.b), cfg.k)
+    with pytest.raises(moe.MoEError):
+        moe.moe_expert_mlp(xd, w, r)
