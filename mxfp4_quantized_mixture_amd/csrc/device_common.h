@@ -20,6 +20,15 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 // fp32 -> bf16 bits, round half to even (finite inputs).
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wavefront wait for all of its
+// outstanding loads (the load counter does not tell loads from stores).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;

@@ -65,6 +65,13 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, const 
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt not waited for)
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but the N most recently issued vector-memory
+// operations have completed (the count is kept in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
 template <int N, typename Fn, int... I>
@@ -293,16 +300,19 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][j][i] = 0.f;
 
-    // Stage i = steps kStage i .. kStage i + kStage - 1, in LDS buffer i % 2.
-    u32x4_t a_cur[kStage][NA], a_nxt[kStage][NA];
+    // Stage i = steps kStage i .. kStage i + kStage - 1: its activation
+    // steps in LDS buffer i % 2, its weight fragments in register slot i % 3.
+    // The weights (read by every pair tile of the expert, mostly from beyond
+    // L2) are loaded two stages ahead, the activations one stage ahead.
+    using AStage = u32x4_t[kStage][NA];
+    AStage a_ring[3];
     const int nst = S / kStage;                         // whole stages; a partial one may follow
 
-    // stage i: activation steps -> LDS buffer i % 2, weights -> a_nxt (steps clamped)
-    auto load_stage = [&](int i) {
+    // stage i's activation steps -> LDS buffer i % 2 (steps clamped)
+    auto load_act = [&](int i) {
 #pragma unroll
         for (int kk = 0; kk < kStage; ++kk) {
-            const uint32_t st = (uint32_t)min(i * kStage + kk, S - 1);
-            const uint32_t so = st * kChunk;
+            const uint32_t so = (uint32_t)min(i * kStage + kk, S - 1) * kChunk;
             uint8_t* slot = lds + (i & 1) * kBufBytes + kk * kSlotBytes;
             // (a wave whose pieces lie past the slot, in the last round, loads
             // a duplicate into its dummy area: no branches in the loop)
@@ -311,17 +321,24 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
                 const bool real = kGemmThreads * c + wave * 64 < kGemmRows * kRowPieces;
                 dma16(bq, gsrc[c] + so, real ? slot + 16 * (kGemmThreads * c + wave * 64) : dummy);
             }
-#pragma unroll
-            for (int a = 0; a < NA; ++a)
-                a_nxt[kk][a] = *reinterpret_cast<const u32x4_t*>(
-                    wq + (aoff[a] + (kPacked ? 1024u : 32u) * st));
         }
     };
-    auto advance_a = [&]() {
+    // stage i's weight fragments -> dst (steps clamped).  Issued after the
+    // activation loads they travel with (the compiler barrier keeps them
+    // there), so waiting until only kALoads operations are outstanding
+    // leaves exactly these in flight.
+    constexpr int kALoads = kStage * NA;
+    auto load_a = [&](int i, AStage& dst) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int kk = 0; kk < kStage; ++kk)
+        for (int kk = 0; kk < kStage; ++kk) {
+            const uint32_t st = (uint32_t)min(i * kStage + kk, S - 1);
 #pragma unroll
-            for (int a = 0; a < NA; ++a) a_cur[kk][a] = a_nxt[kk][a];
+            for (int a = 0; a < NA; ++a)
+                dst[kk][a] = *reinterpret_cast<const u32x4_t*>(
+                    wq + (aoff[a] + (kPacked ? 1024u : 32u) * st));
+        }
     };
     // Products of one stage, software-pipelined over its kStage x NB x NT
     // operand groups (step kk, pair fragment j, term t): group q + 1's B
@@ -339,7 +356,8 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
         fr.lo = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g);
         fr.hi = *reinterpret_cast<const u32x4_t*>(row + 64 * t + 32 * g + 16);
     };
-    auto mfma_frag = [&](int kk, int j, auto tc, const Frag& fr, const int (&as)[NA]) {
+    auto mfma_frag = [&](const AStage& a_cur, int kk, int j, auto tc, const Frag& fr,
+                         const int (&as)[NA]) {
         constexpr int t = decltype(tc)::value;
         const i32x8_t b8 = {(int)fr.lo[0], (int)fr.lo[1], (int)fr.lo[2], (int)fr.lo[3],
                             (int)fr.hi[0], (int)fr.hi[1], (int)fr.hi[2], (int)fr.hi[3]};
@@ -353,9 +371,11 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
                 a8, b8, acc[a][j], 4, 0, 0, as[a], 2 * (t & 1), (int)fr.sw);
         }
     };
-    // nsteps (<= kStage) steps of the stage in buffer buf, first step s0;
-    // after_first() runs once the first group's products are issued
-    auto compute_stage = [&](int buf, int s0, int nsteps, auto&& after_first) {
+    // nsteps (<= kStage) steps of the stage in buffer buf with weights a_cur,
+    // first step s0; after_first() runs once the first group's products are
+    // issued
+    auto compute_stage = [&](int buf, int s0, int nsteps, const AStage& a_cur,
+                             auto&& after_first) {
         constexpr int kGroups = kStage * NB * NT;
         Frag fr[2];
         int as[kStage][NA];
@@ -374,7 +394,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
                         read_frag(buf, q1 / (NB * NT), (q1 / NT) % NB, q1 % NT, fr[q1 & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_frag(kk, j, std::integral_constant<int, t>{}, fr[q & 1], as[kk]);
+                mfma_frag(a_cur, kk, j, std::integral_constant<int, t>{}, fr[q & 1], as[kk]);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (q == 0) {
                     after_first();
@@ -384,25 +404,52 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
         });
     };
 
-    // prologue: weight scales and stage 0 in LDS (one round trip; the
-    // barrier's release waits for the direct loads)
+    // prologue: weight scales and stage 0 in LDS, stage 0's and 1's weights
+    // in registers; wait for all but stage 1's weights (the direct loads
+    // land in LDS before the counter drops)
     copy_weight_scales();
-    load_stage(0);
-    wait_vm_all();
-    __syncthreads();
-    advance_a();
-    // Stage i: products from buffer i % 2, with stage i + 1's loads issued
-    // right after the first group of them (its buffer was last read in stage
-    // i - 1); the barrier at the end waits for the loads, so each has almost
-    // a whole stage to land.
-    for (int i = 0; i < nst; ++i) {
-        compute_stage(i & 1, i * kStage, kStage, [&]() { load_stage(i + 1); });
-        wait_vm_all();
-        __syncthreads();
-        advance_a();
+    load_act(0);
+    load_a(0, a_ring[0]);
+    load_a(1, a_ring[1]);
+    wait_vm<kALoads>();
+    lds_barrier();
+    // Stage i: products from buffer i % 2 and slot i % 3, with stage i + 1's
+    // activations and stage i + 2's weights issued right after the first
+    // group of them (buffer (i + 1) % 2 was last read in stage i - 1, slot
+    // (i + 2) % 3 likewise).  The wait at the end leaves only stage i + 2's
+    // weights in flight: activations get almost one stage to land, weights
+    // almost two.  The loop takes three stages per trip, without branches,
+    // so that every register slot keeps one fixed set of registers.
+    auto run_stage = [&](int i, auto rc) {
+        constexpr int r = decltype(rc)::value;
+        compute_stage(i & 1, i * kStage, kStage, a_ring[r], [&]() {
+            load_act(i + 1);
+            load_a(i + 2, a_ring[(r + 2) % 3]);
+        });
+        wait_vm<kALoads>();
+        lds_barrier();
+    };
+    int i0 = 0;
+    for (; i0 + 3 <= nst; i0 += 3) {
+        run_stage(i0, std::integral_constant<int, 0>{});
+        run_stage(i0 + 1, std::integral_constant<int, 1>{});
+        run_stage(i0 + 2, std::integral_constant<int, 2>{});
     }
-    if (nst * kStage < S)                               // partial last stage
-        compute_stage(nst & 1, nst * kStage, S - nst * kStage, []() {});
+    if (i0 < nst) run_stage(i0, std::integral_constant<int, 0>{});
+    if (i0 + 1 < nst) run_stage(i0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (kStage > 1) {
+        if (nst * kStage < S) {                         // partial last stage, slot nst % 3
+            const int s0 = nst * kStage, ns = S - s0;
+            switch (nst % 3) {
+                case 0: compute_stage(nst & 1, s0, ns, a_ring[0], []() {}); break;
+                case 1: compute_stage(nst & 1, s0, ns, a_ring[1], []() {}); break;
+                default: compute_stage(nst & 1, s0, ns, a_ring[2], []() {}); break;
+            }
+        }
+    }
+    // (the last stages' clamped prefetches may still be in flight; the LDS
+    // is reused below and released at exit)
+    wait_vm_all();
 
     if constexpr (kGateUp) {
         // h = silu(g) * u for features 32 f .. 32 f + 31 (block f of the down

@@ -247,15 +247,6 @@ __device__ __forceinline__ float act_to_f32(uint16_t v, bool is_bf16) {
                    : (float)__builtin_bit_cast(_Float16, v);
 }
 
-// Workgroup barrier ordering LDS accesses only.  __syncthreads() also
-// orders global memory, which makes every wavefront wait for all of its
-// outstanding loads (the load counter does not tell loads from stores).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Stage the unit's rows (pairs row0 .. row0 + nvalid - 1 in sorted order;
 // gathered bf16 x rows for gate/up, contiguous fp16 h rows for down) as NT
 // fp8 terms.  One thread per (row, 32-element block); rows past nvalid and
