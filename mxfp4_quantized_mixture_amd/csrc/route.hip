@@ -363,17 +363,16 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(
 
 // Few tokens (T <= kSmallTokens, T E <= kSmallLogits): one block of 16
 // wavefronts does the whole routing in one launch.
-//  1. Sum the router slices of every (token, expert) logit into LDS (each
-//     thread has the slice loads of four logits in flight at once); rows are
-//     padded to E + 1 floats.
-//  2. Top-k with one 16-lane row per token (wavefront w, row r: token
-//     4 w + r): lane s keeps the best (logit, id) of experts s, s + 16, ...
-//     in registers (insertion into a sorted list of k rounded up to a power
-//     of two; larger logit first, then lower id), and the row's 16 lists are
-//     merged through the DPP crossbar (row shifts by 1, 2, 4, 8, each merging
-//     two lists of disjoint expert sets), leaving the token's list in the
-//     row's last lane.  The order of the selections is the same total order
-//     as repeated argmax.
+//  1. Sum the router slices of every (token, expert) logit into LDS, 16
+//     slice loads in flight per thread (16 slices of one logit, or 4 slices
+//     of four logits when S <= 4); rows are padded to E + 1 floats so that
+//     lanes reading one expert of different tokens hit different banks.
+//  2. Top-k with one lane per token: wavefront w keeps the best (logit, id)
+//     of its slice of experts in registers (insertion into a sorted list of
+//     k rounded up to a power of two; larger logit first, then lower id), and
+//     the 16 lists are merged pairwise through LDS (16 -> 8 -> 4 -> 2 -> 1).
+//     The order of the selections is the same total order as repeated
+//     argmax.
 //  3. Softmax over the k, histogram, scan and stable scatter.
 constexpr int kSmallTokens = 64;
 constexpr int kSmallLogits = 8192;
@@ -423,21 +422,37 @@ __device__ __forceinline__ void topk_merge(float (&av)[K], int (&ai)[K], const f
     }
 }
 
-// (bv, bi) of lane i becomes the merge of its own list with that of lane
-// i - d of its 16-lane row (unchanged where there is none): one step of the
-// row-wise reduction whose four steps leave the whole row's list in lane 15.
-template <int KP, int kCtrl, int kBankMask>
-__device__ __forceinline__ void topk_merge_dpp(float (&bv)[KP], int (&bi)[KP]) {
-    float ov[KP];
-    int oi[KP];
+// Sum the S router slices (S <= kSP) of logits tid, tid + blockDim.x, ...
+// of P [S][n] into lg (row t at t (E + 1)) and logits_out.  kU logits per
+// round with kU * kSP = 16 loads, all issued before any is used: out-of-range
+// slices and logits load a valid address and are discarded (no branches
+// around the loads).
+template <int kSP>
+__device__ __forceinline__ void sum_router_slices(const float* __restrict__ P, int S, int n,
+                                                  int E, float* lg,
+                                                  float* __restrict__ logits_out) {
+    constexpr int kU = 16 / kSP;
+    const int tid = threadIdx.x;
+    for (int i0 = tid; i0 < n; i0 += kU * blockDim.x) {
+        float part[kU][kSP];
 #pragma unroll
-    for (int s = 0; s < KP; ++s) {
-        ov[s] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-            __builtin_bit_cast(int, -__builtin_inff()), __builtin_bit_cast(int, bv[s]), kCtrl, 0xF,
-            kBankMask, false));
-        oi[s] = __builtin_amdgcn_update_dpp(0x7FFFFFFF, bi[s], kCtrl, 0xF, kBankMask, false);
+        for (int u = 0; u < kU; ++u) {
+            const int i = min(i0 + u * (int)blockDim.x, n - 1);
+#pragma unroll
+            for (int sp = 0; sp < kSP; ++sp) part[u][sp] = P[(int64_t)min(sp, S - 1) * n + i];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = i0 + u * blockDim.x;
+            float acc = part[u][0];
+#pragma unroll
+            for (int sp = 1; sp < kSP; ++sp) acc = sp < S ? acc + part[u][sp] : acc;
+            if (i < n) {
+                lg[i + i / E] = acc;
+                if (logits_out) logits_out[i] = acc;
+            }
+        }
     }
-    topk_merge<KP>(bv, bi, ov, oi);
 }
 
 template <int K>
@@ -447,7 +462,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
     constexpr int k = K;
     constexpr int KP = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : 8;   // list length, a power of two
-    __shared__ float lg[kSmallLogits + kSmallTokens];   // logits [T][E + 1]
+    // logits [T][E + 1], later the merge lists: values [8][KP][64], ids after them
+    __shared__ float lg[kSmallLogits + kSmallTokens];
     __shared__ int cnt[kMaxE];
     __shared__ int pair_e[kSmallTokens * kMaxK];
     __shared__ int seg_base[8 * kMaxE];
@@ -455,65 +471,66 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     __shared__ int wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < kMaxE; i += blockDim.x) cnt[i] = 0;
-    constexpr int kMaxS = 16;
-    constexpr int kLogitsPerRound = 4;
     const int n = T * E;
-    for (int i0 = tid; i0 < n; i0 += kLogitsPerRound * blockDim.x) {
-        float part[kLogitsPerRound][kMaxS];
-#pragma unroll
-        for (int u = 0; u < kLogitsPerRound; ++u) {
-            const int i = i0 + u * blockDim.x;
-#pragma unroll
-            for (int sp = 0; sp < kMaxS; ++sp)
-                part[u][sp] = (i < n && sp < S) ? P[(int64_t)sp * n + i] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kLogitsPerRound; ++u) {
-            const int i = i0 + u * blockDim.x;
-            float acc = part[u][0];
-#pragma unroll
-            for (int sp = 1; sp < kMaxS; ++sp)
-                if (sp < S) acc += part[u][sp];
-            if (i < n) {
-                lg[i + i / E] = acc;                  // row t starts at t (E + 1)
-                if (logits_out) logits_out[i] = acc;
-            }
-        }
-    }
+    if (S <= 4)
+        sum_router_slices<4>(P, S, n, E, lg, logits_out);
+    else
+        sum_router_slices<16>(P, S, n, E, lg, logits_out);
     __syncthreads();
 
-    // 2. top-k, one 16-lane row per token
-    const int t = 4 * wave + (lane >> 4), sl = lane & 15;
-    if (4 * wave < T) {                           // (wave-uniform: the DPP steps need every lane)
-        float bv[KP];
-        int bi[KP];
+    // 2. top-k, lane = token
+    float bv[KP];
+    int bi[KP];
 #pragma unroll
-        for (int s = 0; s < KP; ++s) {
-            bv[s] = -__builtin_inff();
-            bi[s] = 0x7FFFFFFF;                   // ranks after every real (logit, id)
-        }
+    for (int s = 0; s < KP; ++s) {
+        bv[s] = -__builtin_inff();
+        bi[s] = 0x7FFFFFFF;                       // ranks after every real (logit, id)
+    }
+    const int t = lane;
+    {
+        const int eg = (E + 15) / 16;
+        const int e0 = wave * eg, e1 = min(E, e0 + eg);
         if (t < T)
-            for (int e = sl; e < E; e += 16) topk_insert<KP>(bv, bi, lg[t * (E + 1) + e], e);
-        topk_merge_dpp<KP, 0x111, 0xF>(bv, bi);   // row_shr:1
-        topk_merge_dpp<KP, 0x112, 0xF>(bv, bi);   // row_shr:2
-        topk_merge_dpp<KP, 0x114, 0xE>(bv, bi);   // row_shr:4
-        topk_merge_dpp<KP, 0x118, 0xC>(bv, bi);   // row_shr:8
-        // 3. softmax over the k selected logits (bv[0] is the largest)
-        if (sl == 15 && t < T) {
-            float ex[K];
-            float den = 0.f;
+            for (int e = e0; e < e1; ++e) topk_insert<KP>(bv, bi, lg[t * (E + 1) + e], e);
+    }
+    float* lv = lg;                               // [8][KP][64]
+    int* li = reinterpret_cast<int*>(lg + 8 * KP * 64);
+    for (int half = 8; half >= 1; half >>= 1) {
+        __syncthreads();                          // logits / previous lists no longer read
+        if (wave >= half && wave < 2 * half) {
 #pragma unroll
-            for (int s = 0; s < K; ++s) {
-                ex[s] = expf(bv[s] - bv[0]);
-                den += ex[s];
+            for (int s = 0; s < KP; ++s) {
+                lv[((wave - half) * KP + s) * 64 + lane] = bv[s];
+                li[((wave - half) * KP + s) * 64 + lane] = bi[s];
             }
+        }
+        __syncthreads();
+        if (wave < half && t < T) {
+            float ov[KP];
+            int oi[KP];
 #pragma unroll
-            for (int s = 0; s < K; ++s) {
-                const int e = bi[s] < E ? bi[s] : E - 1;       // only with non-finite logits
-                ids[(int64_t)t * k + s] = e;
-                wts[(int64_t)t * k + s] = ex[s] / den;
-                pair_e[t * k + s] = e;
+            for (int s = 0; s < KP; ++s) {
+                ov[s] = lv[(wave * KP + s) * 64 + lane];
+                oi[s] = li[(wave * KP + s) * 64 + lane];
             }
+            topk_merge<KP>(bv, bi, ov, oi);
+        }
+    }
+    // 3. softmax over the k selected logits (bv[0] is the largest)
+    if (wave == 0 && t < T) {
+        float ex[K];
+        float den = 0.f;
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            ex[s] = expf(bv[s] - bv[0]);
+            den += ex[s];
+        }
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            const int e = bi[s] < E ? bi[s] : E - 1;       // only with non-finite logits
+            ids[(int64_t)t * k + s] = e;
+            wts[(int64_t)t * k + s] = ex[s] / den;
+            pair_e[t * k + s] = e;
         }
     }
     __syncthreads();
