@@ -61,9 +61,10 @@ def packed_ok(cfg) -> bool:
     return cfg.D % 64 == 0 and cfg.F % 64 == 0 and cfg.D <= 3840 and cfg.F <= 2944
 
 
-def read_traffic(kernel: str, workload: str, source: str):
+def read_traffic(kernel: str, workload: str, source: str, layout: str):
     """HBM bytes per dispatch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source (else None)."""
+    was taken on the current kernel source with the same weight layout (else
+    None)."""
     path = os.path.join(ROOT, "profiles", "%s.%s.traffic.txt" % (kernel, workload))
     src = os.path.join(ROOT, "mxfp4_quantized_mixture_amd", "csrc", source)
     if not os.path.exists(path):
@@ -74,7 +75,7 @@ def read_traffic(kernel: str, workload: str, source: str):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != digest:
+    if fields.get("kernel_source_sha256") != digest or fields.get("weight_layout") != layout:
         return None
     try:
         return float(fields["hbm_bytes_per_dispatch"])
@@ -186,6 +187,7 @@ def main() -> int:
 
     xd, wrd, bd = bf16(x), torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)
     packed = args.layout == "packed" or (args.layout == "auto" and packed_ok(cfg))
+    layout = "packed" if packed else "row-major"
     base = moe.ExpertWeights.quantize(bf16(w13), bf16(w2), packed=packed)
     copies = [base] + [moe.ExpertWeights(base.w13_q.clone(), base.w13_s.clone(),
                                          base.w2_q.clone(), base.w2_s.clone(), packed)
@@ -248,11 +250,11 @@ def main() -> int:
         layer_roof = {"bound": "mfma", "achieved": layer, "peak": FP8_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": layer / FP8_PEAK_TFLOPS}
     if decode:
-        roof["kernel"] = "expert_stream_kernel<gate_up>"
-        roof["traffic"] = read_traffic("gateup", cfg.name, "expert_mlp.hip")
+        roof["kernel"] = "expert_stream_kernel<gate_up%s>" % (",packed" if packed else "")
+        roof["traffic"] = read_traffic("gateup", cfg.name, "expert_mlp.hip", layout)
     else:
-        roof["kernel"] = "expert_gemm_kernel<gate_up>"
-        roof["traffic"] = read_traffic("gateup_gemm", cfg.name, "expert_gemm.hip")
+        roof["kernel"] = "expert_gemm_kernel<gate_up%s>" % (",packed" if packed else "")
+        roof["traffic"] = read_traffic("gateup_gemm", cfg.name, "expert_gemm.hip", layout)
     roof["algorithmic_per_launch"] = work["gateup_bytes"] if decode else work["gateup_flops"]
     roof["avg_launch_ms"] = gateup_ms
 
