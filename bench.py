@@ -108,31 +108,38 @@ def cpu_baseline(cfg, inp, tokens) -> dict:
 
 
 def bench_quantize(cfg, args, moe, torch, dev) -> int:
-    """mxfp4_quantize on the workload's W13 (E * 2F rows of D bf16), both
-    roundings; HBM bytes = 2 B read per element + 0.5 + 1/32 B written."""
+    """mxfp4_quantize of all the workload's expert weights, W13 [E*2F, D] and
+    W2 [E*D, F] bf16 (one call each per step), both roundings; HBM bytes =
+    2 B read per element + 0.5 + 1/32 B written."""
     from synth import moe_inputs as MI
-    w13, _ = MI.gen_experts(cfg, args.seed, threads=16)
-    w = torch.from_numpy(w13.reshape(-1, cfg.D).view(np.int16)).to(dev).view(torch.bfloat16)
-    rows, K = w.shape
-    nbytes = rows * K * 2 + rows * K // 2 + rows * K // 32
+    w13, w2 = MI.gen_experts(cfg, args.seed, threads=16)
+    mats = [torch.from_numpy(a.reshape(-1, a.shape[-1]).view(np.int16)).to(dev).view(torch.bfloat16)
+            for a in (w13, w2)]
+    del w13, w2
+    elems = sum(m.numel() for m in mats)
+    nbytes = elems * 2 + elems // 2 + elems // 32
     out = {}
     for name, kw in (("nearest_even", {}), ("stochastic", {"stochastic": True, "seed": 1})):
+        rule = moe.SCALE_CEIL_DIV6 if kw else moe.SCALE_FLOOR_DIV6
         for _ in range(max(args.warmup // 10, 2)):
-            moe.mxfp4_quantize(w, moe.SCALE_CEIL_DIV6 if kw else moe.SCALE_FLOOR_DIV6, **kw)
+            for m in mats:
+                moe.mxfp4_quantize(m, rule, **kw)
         n = max(args.steps // 20, 5)
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
         for _ in range(n):
-            moe.mxfp4_quantize(w, moe.SCALE_CEIL_DIV6 if kw else moe.SCALE_FLOOR_DIV6, **kw)
+            for m in mats:
+                moe.mxfp4_quantize(m, rule, **kw)
         stop.record()
         torch.cuda.synchronize()
         ms = start.elapsed_time(stop) / n
         out[name] = {"ms": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                      "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    print(json.dumps({"metric": "mxfp4_quantize HBM GB/s", "workload": cfg.name + " W13",
-                      "rows": rows, "K": K, "bytes_per_call": nbytes, "calls": n,
-                      "results": out}), flush=True)
+    print(json.dumps({"metric": "mxfp4_quantize HBM GB/s",
+                      "workload": "%s: all %d experts' W13 and W2" % (cfg.name, cfg.E),
+                      "matrices": [list(m.shape) for m in mats], "bytes_per_step": nbytes,
+                      "steps": n, "results": out}), flush=True)
     return 0
 
 
@@ -150,7 +157,7 @@ def main() -> int:
                     help="expert weight code layout (default: packed where the kernels take it)")
     ap.add_argument("--quantize", action="store_true",
                     help="time mxfp4_quantize (nearest-even and stochastic rounding) on the "
-                         "workload's W13 instead of the layer")
+                         "workload's expert weights (W13 and W2) instead of the layer")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a kernel of known traffic)")
