@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kStreamWaves = 8;
-constexpr int kMaxWaveTiles = 4;       // tiles a wavefront owns (outputs held in registers)
+constexpr int kMaxWaveTiles = 4;       // tile outputs a wavefront holds in registers
 
 // Staged activations.  The weights enter the matrix cores exactly as stored
 // (E2M1 codes + E8M0 block scales, v_mfma_scale_f32_16x16x128_f8f6f4 with an
@@ -546,9 +546,12 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
         lds_barrier();                         // not __syncthreads: the weight loads stay in flight
 
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc_gate = {0.f, 0.f, 0.f, 0.f};
-        // Tile results stay in registers until the wave has issued its last
-        // load: on gfx9 the vector memory counter also covers stores, so an
-        // early store would make later load waits wait for its write too.
+        // The first kMaxWaveTiles tile results stay in registers until the
+        // wave has issued its last load: on gfx9 the vector memory counter
+        // also covers stores, so an early store makes later load waits wait
+        // for its write too (measured: 1.5 us per launch at 3 tiles per
+        // wave).  Further tiles (many tiles per wave, when blocks per expert
+        // are few) are stored as soon as they are computed.
         typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
         typedef typename std::conditional<kGateUp, f16x4_t, f32x4_t>::type OutT;
         OutT obuf[kMaxWaveTiles];
@@ -561,9 +564,19 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
             } else {
                 res = acc;
             }
+            if (j < kMaxWaveTiles) {
 #pragma unroll
-            for (int jj = 0; jj < kMaxWaveTiles; ++jj)
-                if (jj == j) obuf[jj] = res;
+                for (int jj = 0; jj < kMaxWaveTiles; ++jj)
+                    if (jj == j) obuf[jj] = res;
+            } else if (m < nvalid) {
+                const int tile = a + wave + j * kStreamWaves;
+                if constexpr (kGateUp)
+                    *reinterpret_cast<OutT*>(static_cast<_Float16*>(out) + (size_t)(row0 + m) * F +
+                                             tile * 16 + 4 * g) = res;
+                else
+                    *reinterpret_cast<OutT*>(static_cast<float*>(out) + (size_t)(row0 + m) * D +
+                                             tile * 16 + 4 * g) = res;
+            }
         };
         auto consume = [&](const WBatch<NB>& W, int s) {
             if (s % seg == 0) {               // tile switch: commit its scales, fetch the next's
@@ -680,15 +693,13 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
 }
 
 // Blocks per expert for the streaming kernels: about 256 blocks in all (one
-// per CU of MI355X) and at least 2 per expert, so untouched experts' CUs are
-// reused by the dispatcher; at least 8 tiles (one per wavefront) per block
-// where possible, and never more than kMaxWaveTiles per wavefront.
+// per CU of MI355X, so every block runs in the first round) and at least 2
+// per expert, so untouched experts' CUs are reused by the dispatcher; at
+// least 8 tiles (one per wavefront) per block where possible.
 static int stream_blocks_per_expert(int E, int ntiles) {
     int bpe = (256 + E - 1) / E;
     if (bpe < 2) bpe = 2;
     if (bpe > ntiles / kStreamWaves) bpe = ntiles / kStreamWaves;
-    const int min_bpe = (ntiles + kStreamWaves * kMaxWaveTiles - 1) / (kStreamWaves * kMaxWaveTiles);
-    if (bpe < min_bpe) bpe = min_bpe;
     return bpe < 1 ? 1 : bpe;
 }
 
