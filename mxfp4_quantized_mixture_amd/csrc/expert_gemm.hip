@@ -394,7 +394,11 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
                         read_frag(buf, q1 / (NB * NT), (q1 / NT) % NB, q1 % NT, fr[q1 & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_frag(a_cur, kk, j, std::integral_constant<int, t>{}, fr[q & 1], as[kk]);
+                // (a pair fragment past the tile's pairs, as in an expert's
+                // last tile, has no products to compute: its results are
+                // never stored; the branch is uniform in the wavefront)
+                if (32 * (wp * NB + j) < nvalid)
+                    mfma_frag(a_cur, kk, j, std::integral_constant<int, t>{}, fr[q & 1], as[kk]);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (q == 0) {
                     after_first();
