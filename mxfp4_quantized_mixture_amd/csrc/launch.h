@@ -17,6 +17,7 @@ hipError_t launch_pack(const uint8_t* q, int64_t rows, int64_t K, uint8_t* out,
 struct RoutePlan {
     int T, D, E, k;
     int token_tiles;   // 16-token tiles per router block
+    int expert_tiles;  // 16-expert tiles per router block
     int splits;        // slices of the router contraction (partial logits summed in order)
     int chunks;        // token chunks of the top-k / histogram pass
     size_t off_logits, off_chunk_counts, off_chunk_base, ws_bytes;

@@ -36,10 +36,13 @@ constexpr int kMaxE = 256;
 // the top 16 bits of w, mid the top 16 bits of the (exact) residual, and lo
 // the remaining at most 8 significant bits.  The activations are bf16, so the
 // three 16x16x32 bf16 products accumulate x . w with fp32 rounding only.
-// Grid: 16-expert tiles x (16 * TT)-token tiles x S slices of the
+// Grid: (16 * NE)-expert tiles x (16 * TT)-token tiles x S slices of the
 // contraction; each block's 4 wavefronts split its slice further and are
 // summed through LDS in a fixed order.  Slice s writes its partial tile to
 // P[s]; slice 0 adds the bias.  The top-k kernel sums the S slices in order.
+// A block's NE expert tiles share its activation loads (x is read once per
+// expert tile group, not once per 16 experts); KB K-steps' loads are issued
+// together.
 constexpr int kRouterWaves = 4;
 
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8_t& hi, bf16x8_t& mid,
@@ -65,35 +68,44 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8_t& hi, b
     lo = as_bf16x8(l);
 }
 
-template <int TT>
+template <int TT, int NE, int KB>
 __global__ __launch_bounds__(kRouterWaves * 64) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
     float* __restrict__ P, int T, int D, int E, int S) {
-    __shared__ f32x4_t red[kRouterWaves][TT][64];
+    __shared__ f32x4_t red[kRouterWaves][NE * TT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * TT, sl = blockIdx.z;
+    const int e0 = blockIdx.x * 16 * NE, t0 = blockIdx.y * 16 * TT, sl = blockIdx.z;
     const int nk = D / 32;
     const int part = sl * kRouterWaves + wave, parts = S * kRouterWaves;
     const int k_beg = (int)((int64_t)nk * part / parts), k_end = (int)((int64_t)nk * (part + 1) / parts);
-    const int e = e0 + m;
-    const bool eok = e < E;
-    const float* wrow = wr + (int64_t)(eok ? e : 0) * D;
-    f32x4_t acc[TT];
+    const float* wrow[NE];
+    bool eok[NE];
 #pragma unroll
-    for (int u = 0; u < TT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int KB = 4;                       // K-steps whose loads are issued together
+    for (int n = 0; n < NE; ++n) {
+        const int e = e0 + 16 * n + m;
+        eok[n] = e < E;
+        wrow[n] = wr + (int64_t)(eok[n] ? e : 0) * D;
+    }
+    f32x4_t acc[NE][TT];
+#pragma unroll
+    for (int n = 0; n < NE; ++n)
+#pragma unroll
+        for (int u = 0; u < TT; ++u) acc[n][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int kk = k_beg; kk < k_end; kk += KB) {
-        float4 wa[KB], wb[KB];
+        float4 wa[KB][NE], wb[KB][NE];
         u32x4_t xv[KB][TT];
 #pragma unroll
         for (int h = 0; h < KB; ++h) {
             const int off = (kk + h) * 32 + 8 * g;
             const bool kok = kk + h < k_end;
-            wa[h] = wb[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kok && eok) {
-                wa[h] = *reinterpret_cast<const float4*>(wrow + off);
-                wb[h] = *reinterpret_cast<const float4*>(wrow + off + 4);
+#pragma unroll
+            for (int n = 0; n < NE; ++n) {
+                wa[h][n] = wb[h][n] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (kok && eok[n]) {
+                    wa[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off);
+                    wb[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off + 4);
+                }
             }
 #pragma unroll
             for (int u = 0; u < TT; ++u) {
@@ -105,33 +117,39 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_logits_kernel(
 #pragma unroll
         for (int h = 0; h < KB; ++h) {
             if (kk + h < k_end) {
-                const float w[8] = {wa[h].x, wa[h].y, wa[h].z, wa[h].w,
-                                    wb[h].x, wb[h].y, wb[h].z, wb[h].w};
-                bf16x8_t hi, mid, lo;
-                split3_bf16(w, hi, mid, lo);
 #pragma unroll
-                for (int u = 0; u < TT; ++u) {
-                    const bf16x8_t xb = as_bf16x8(xv[h][u]);
-                    acc[u] = mfma_bf16(hi, xb, acc[u]);
-                    acc[u] = mfma_bf16(mid, xb, acc[u]);
-                    acc[u] = mfma_bf16(lo, xb, acc[u]);
+                for (int n = 0; n < NE; ++n) {
+                    const float w[8] = {wa[h][n].x, wa[h][n].y, wa[h][n].z, wa[h][n].w,
+                                        wb[h][n].x, wb[h][n].y, wb[h][n].z, wb[h][n].w};
+                    bf16x8_t hi, mid, lo;
+                    split3_bf16(w, hi, mid, lo);
+#pragma unroll
+                    for (int u = 0; u < TT; ++u) {
+                        const bf16x8_t xb = as_bf16x8(xv[h][u]);
+                        acc[n][u] = mfma_bf16(hi, xb, acc[n][u]);
+                        acc[n][u] = mfma_bf16(mid, xb, acc[n][u]);
+                        acc[n][u] = mfma_bf16(lo, xb, acc[n][u]);
+                    }
                 }
             }
         }
     }
 #pragma unroll
-    for (int u = 0; u < TT; ++u) red[wave][u][lane] = acc[u];
+    for (int n = 0; n < NE; ++n)
+#pragma unroll
+        for (int u = 0; u < TT; ++u) red[wave][n * TT + u][lane] = acc[n][u];
     __syncthreads();
-    // lane holds C[expert 4g + r][token m] of each token tile
+    // lane holds C[expert 4g + r][token m] of each (expert, token) tile
     float* Ps = P + (int64_t)sl * T * E;
-    for (int u = wave; u < TT; u += kRouterWaves) {
-        f32x4_t sum = red[0][u][lane];
-        for (int w2 = 1; w2 < kRouterWaves; ++w2) sum += red[w2][u][lane];
+    for (int nu = wave; nu < NE * TT; nu += kRouterWaves) {
+        const int n = nu / TT, u = nu - n * TT;
+        f32x4_t sum = red[0][nu][lane];
+        for (int w2 = 1; w2 < kRouterWaves; ++w2) sum += red[w2][nu][lane];
         const int t = t0 + 16 * u + m;
         if (t < T) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int ee = e0 + 4 * g + r;
+                const int ee = e0 + 16 * n + 4 * g + r;
                 if (ee < E) Ps[(int64_t)t * E + ee] = sum[r] + ((br && sl == 0) ? br[ee] : 0.f);
             }
         }
@@ -607,10 +625,17 @@ RoutePlan plan_route(int T, int D, int E, int k) {
     RoutePlan p{};
     p.T = T; p.D = D; p.E = E; p.k = k;
     p.token_tiles = T <= 64 ? 1 : 4;           // 16-token tiles per router block
-    const int tiles = ((E + 15) / 16) * ((T + 16 * p.token_tiles - 1) / (16 * p.token_tiles));
-    // split the contraction over blocks until ~128 blocks are busy (at most 16
-    // slices, and each wavefront keeps at least one 32-column step)
-    int S = (128 + tiles - 1) / tiles;
+    // 16-expert tiles per router block: one for decode (latency: many small
+    // blocks), several for long batches (each block reads its x rows once for
+    // all of them)
+    p.expert_tiles = T <= 64 ? 1 : (E > 32 ? 4 : 2);
+    const int tiles = ((E + 16 * p.expert_tiles - 1) / (16 * p.expert_tiles)) *
+                      ((T + 16 * p.token_tiles - 1) / (16 * p.token_tiles));
+    // split the contraction over blocks until ~128 blocks (decode) or ~512
+    // blocks (long batches: two per CU) are busy, at most 16 slices, and each
+    // wavefront keeps at least one 32-column step
+    const int want = T <= 64 ? 128 : 512;
+    int S = (want + tiles - 1) / tiles;
     const int max_s = (D / 32) / kRouterWaves;
     if (S > max_s) S = max_s;
     if (S > 16) S = 16;
@@ -635,14 +660,18 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
     float* P = reinterpret_cast<float*>(base + p.off_logits);
     int32_t* chunk_counts = reinterpret_cast<int32_t*>(base + p.off_chunk_counts);
     int32_t* chunk_base = reinterpret_cast<int32_t*>(base + p.off_chunk_base);
-    if (p.token_tiles == 1) {
-        dim3 g((p.E + 15) / 16, (p.T + 15) / 16, p.splits);
-        hipLaunchKernelGGL(router_logits_kernel<1>, g, dim3(kRouterWaves * 64), 0, stream, x, wr,
-                           br, P, p.T, p.D, p.E, p.splits);
-    } else {
-        dim3 g((p.E + 15) / 16, (p.T + 63) / 64, p.splits);
-        hipLaunchKernelGGL(router_logits_kernel<4>, g, dim3(kRouterWaves * 64), 0, stream, x, wr,
-                           br, P, p.T, p.D, p.E, p.splits);
+    {
+        const int et = 16 * p.expert_tiles, tt = 16 * p.token_tiles;
+        const dim3 g((p.E + et - 1) / et, (p.T + tt - 1) / tt, p.splits);
+        if (p.token_tiles == 1)
+            hipLaunchKernelGGL((router_logits_kernel<1, 1, 4>), g, dim3(kRouterWaves * 64), 0,
+                               stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
+        else if (p.expert_tiles == 2)
+            hipLaunchKernelGGL((router_logits_kernel<4, 2, 4>), g, dim3(kRouterWaves * 64), 0,
+                               stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
+        else
+            hipLaunchKernelGGL((router_logits_kernel<4, 4, 2>), g, dim3(kRouterWaves * 64), 0,
+                               stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
     }
     if (p.T <= kSmallTokens && p.T * p.E <= kSmallLogits) {
         switch (p.k) {
