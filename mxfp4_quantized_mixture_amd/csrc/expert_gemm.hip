@@ -7,20 +7,34 @@
 // (its routed pairs in sorted order):  [G | U] = X_e W13_e^T,
 // H = silu(G) * U,  Y = H W2_e^T;  the weighted combine follows.
 //
-// Matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4.  The MXFP4 weights are its
-// A operand exactly as stored (E2M1 codes, E8M0 block scales as the hardware
-// scale operand); the activations are its B operand as fp8 (E4M3) residual
-// terms with their own E8M0 block scales: x (bf16) as 2 terms, which is exact,
-// and h as 3 terms, produced directly by the gate/up epilogue.
+// Gate/up: v_mfma_scale_f32_32x32x64_f8f6f4.  The MXFP4 weights are its A
+// operand exactly as stored (E2M1 codes, E8M0 block scales as the hardware
+// scale operand); x is its B operand as 2 fp8 (E4M3) residual terms with their
+// own E8M0 block scales, which is exact for bf16.  The epilogue writes
+// h = silu(g) * u as fp16 rows.
 //
-// Operand layouts of the 32x32x64 product (lane l, n = l % 32, g = l / 32):
-//   A: row n, K = 32 g .. 32 g + 31 (one MXFP4 block, low nibble first) in
-//      the first 16 bytes; scale = that block's E8M0 byte.
-//   B: column n, bytes 0..15 = K 16 g .. 16 g + 15, bytes 16..31 =
-//      K 32 + 16 g .. + 15; scale = K-block g of column n.
-//   C: element i = row 8 (i / 4) + 4 g + i % 4, column n.
+// Down: v_mfma_f32_32x32x16_f16 on h (fp16, as stored) and the W2 codes
+// converted to fp16 in registers (v_cvt_scalef32_pk_f16_fp4, one conversion
+// per code per tile).  A W2 row's codes are converted with the scales
+// 2^(b - bmax + 13), b the block's scale byte and bmax the row's largest, so
+// every code of a block within 36 binades of the row's largest is exact in
+// fp16 (at most 6 * 2^13); the row's fp32 sums are then scaled by
+// 2^(bmax - 140).  Codes of blocks further below keep fp16's rounding, an
+// error under 2^-37 of the row's largest weight.
 //
-// Activation term rows.  A row of K elements (K % 64 == 0) is S = K / 64
+// Operand layouts (lane l, n = l % 32, g = l / 32):
+//   32x32x64 f8f6f4:
+//     A: row n, K = 32 g .. 32 g + 31 (one MXFP4 block, low nibble first) in
+//        the first 16 bytes; scale = that block's E8M0 byte.
+//     B: column n, bytes 0..15 = K 16 g .. 16 g + 15, bytes 16..31 =
+//        K 32 + 16 g .. + 15; scale = K-block g of column n.
+//   32x32x16 f16: A row n / B column n, elements 8 g .. 8 g + 7.  A lane's
+//     16 code bytes (K = 32 g .. 32 g + 31 of a 64-wide step) feed four
+//     products, product j taking elements 32 g + 8 j .. + 7; the h operand is
+//     read in the same order.
+//   C (both): element i = row 8 (i / 4) + 4 g + i % 4, column n.
+//
+// Activation term rows (x).  A row of K elements (K % 64 == 0) is S = K / 64
 // steps of term_chunk(NT) = NT * 64 + 16 bytes.  Term t's 64 codes sit at
 // 64 t in B operand order: [lane group 0: elements 0..15 of block 2s,
 // elements 0..15 of block 2s+1][lane group 1: elements 16..31 of block 2s,
@@ -45,6 +59,9 @@ constexpr int kScaleIters = 8;      // weight-scale copy: K <= 64 lanes x 16 byt
 static_assert(64 * 16 * kScaleIters == kGemmMaxContraction, "scale copy covers every K");
 
 __host__ __device__ constexpr int term_chunk(int NT) { return NT * 64 + 16; }
+// LDS row pitch of a 64-element fp16 h step: 128 bytes plus a 16-byte pad
+// (an odd number of 16-byte units keeps the operand reads conflict free)
+constexpr int kHPitch = 144;
 
 // Direct global -> LDS load of 16 bytes per lane: lane l's 16 bytes at
 // base + voff land at LDS byte lds_base + 16 l (lds_base wave-uniform).
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 // kWaveFrags output fragments (WR = 4: one block per CU with 128 x 128
 // accumulator tiles; WR = 2: two blocks per CU with 128 x 64 tiles):
 //   gate/up: 2 feature fragments -> 4 A fragments (their gate and up rows),
-//            epilogue h = silu(g) * u written as 3-term rows;
+//            epilogue h = silu(g) * u written as fp16 rows;
 //   down:    4 output fragments -> 4 A fragments, epilogue y (fp32).
 // The contraction runs in stages of kStage 64-wide steps (128 per stage
 // when LDS allows): activations go global -> registers -> one of two LDS
@@ -188,16 +205,21 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     const uint8_t* __restrict__ bq, const int32_t* __restrict__ sorted, int k,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
-    uint8_t* __restrict__ hq, float* __restrict__ y) {
-    constexpr int NT = kGateUp ? 2 : 3;                 // activation terms
+    _Float16* __restrict__ h, float* __restrict__ y) {
+    constexpr int NT = 2;                               // x terms (gate/up)
     constexpr int NA = 4;                               // A fragments per wave
     constexpr int kGemmThreads = 64 * WR * WP;
     constexpr int NB = 4 / WP;                          // B fragments (32 pairs) per wave
+    static_assert(WR <= 4 && WR * WP <= 8, "wavefront layout");
     constexpr int kWaveFrags = kGateUp ? 2 : 4;         // output fragments per wave
-    constexpr int kChunk = term_chunk(NT);
+    // A step of an activation row: kStepBytes in global memory (x: the
+    // terms and scales of one step chunk; h: 64 fp16 values), kChunk in LDS
+    // (h: plus a pad unit, loaded as a copy of the step's last 16 bytes).
+    constexpr int kChunk = kGateUp ? term_chunk(NT) : kHPitch;
+    constexpr int kStepBytes = kGateUp ? kChunk : 128;
     // LDS slot of one step: the 128 rows' step chunks, row-major.  The row
-    // pitch kChunk = 16 (NT * 4 + 1) bytes keeps both the staging copy and
-    // the operand reads (lanes n = 0..15 at 16-byte units 9 n or 13 n mod 16)
+    // pitch kChunk = 144 bytes (9 units of 16) keeps both the staging copy
+    // and the operand reads (lanes n = 0..15 at 16-byte units 9 n mod 16)
     // free of bank conflicts.
     constexpr int kSlotBytes = kGemmRows * kChunk;
     constexpr int kRowPieces = kChunk / 16;
@@ -205,6 +227,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     constexpr int kBufBytes = kStage * kSlotBytes;      // one stage of activation steps
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int s_src[kGemmRows];
+    __shared__ int s_rmax[4][NA][32];                   // (down) bmax of each A fragment row
 
     // Work item L = m-tile * ntl + column tile.  The dispatcher deals blocks
     // to the 8 XCDs round robin (block b -> XCD b % 8), each XCD with its own
@@ -223,7 +246,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     const int wr = wave / WP, wp = wave % WP;           // this wave's row group and pair group
     const int n = lane & 31, g = lane >> 5;
     const int S = K / 64;
-    const size_t RB = (size_t)S * kChunk;               // bytes per activation term row
+    const size_t RB = (size_t)S * kStepBytes;           // bytes per activation row
 
     // Rows past the tile's pairs repeat its last pair (their results are not stored).
     if (tid < kGemmRows) {
@@ -289,7 +312,8 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     for (int c = 0; c < kPieces; ++c) {
         const int p = min(tid + kGemmThreads * c, kGemmRows * kRowPieces - 1);
         const int r = p / kRowPieces;
-        gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * (p - r * kRowPieces));
+        const int piece = min(p - r * kRowPieces, kStepBytes / 16 - 1);
+        gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * piece);
     }
 
     f32x16_t acc[NA][NB];
@@ -312,7 +336,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     auto load_act = [&](int i) {
 #pragma unroll
         for (int kk = 0; kk < kStage; ++kk) {
-            const uint32_t so = (uint32_t)min(i * kStage + kk, S - 1) * kChunk;
+            const uint32_t so = (uint32_t)min(i * kStage + kk, S - 1) * kStepBytes;
             uint8_t* slot = lds + (i & 1) * kBufBytes + kk * kSlotBytes;
             // (a wave whose pieces lie past the slot, in the last round, loads
             // a duplicate into its dummy area: no branches in the loop)
@@ -376,6 +400,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     // issued
     auto compute_stage = [&](int buf, int s0, int nsteps, const AStage& a_cur,
                              auto&& after_first) {
+      if constexpr (kGateUp) {
         constexpr int kGroups = kStage * NB * NT;
         Frag fr[2];
         int as[kStage][NA];
@@ -406,6 +431,70 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
                 }
             }
         });
+      } else {
+        // Group q = (step kk, sub-step jj, pair fragment j): the NA products
+        // over elements 8 jj .. 8 jj + 7 of each lane's 32.  The A fragments
+        // of sub-step jj + 1 are converted once sub-step jj's last products
+        // are issued (they run meanwhile), and group q + 1's h operand is
+        // read from LDS during group q.
+        constexpr int kGroups = kStage * 4 * NB;
+        float sc[kStage][NA];                           // conversion scales (rewritten bytes)
+#pragma unroll
+        for (int kk = 0; kk < kStage; ++kk)
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+                sc[kk][a] = __builtin_bit_cast(float, (uint32_t)my_sc[a * K + 2 * min(s0 + kk, S - 1)] << 23);
+        f16x8_t af[NA], bf[2];
+        auto convert = [&](auto kc, auto jc, f16x8_t(&dst)[NA]) {
+            constexpr int kk = decltype(kc)::value, jj = decltype(jc)::value;
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                const uint32_t w = a_cur[kk][a][jj];
+                // byte i's two codes (low nibble first) -> elements 2 i, 2 i + 1
+                const u32x4_t v = {
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[kk][a], 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[kk][a], 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[kk][a], 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[kk][a], 3))};
+                dst[a] = __builtin_bit_cast(f16x8_t, v);
+            }
+        };
+        auto read_b = [&](int kk, int j, int jj, f16x8_t& dst) {
+            // pair 32 j + n of the step: elements 32 g + 8 jj .. + 7
+            const uint8_t* row = lds + buf * kBufBytes + kk * kSlotBytes + (32 * (wp * NB + j) + n) * kChunk;
+            dst = *reinterpret_cast<const f16x8_t*>(row + 64 * g + 16 * jj);
+        };
+        convert(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, af);
+        read_b(0, 0, 0, bf[0]);
+        static_for<kGroups>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int u = q / NB, kk = u / 4, j = q % NB;
+            if (kk < nsteps) {
+                if constexpr (q + 1 < kGroups) {
+                    constexpr int q1 = q + 1;
+                    if (q1 / (4 * NB) < nsteps) read_b(q1 / (4 * NB), q1 % NB, (q1 / NB) % 4, bf[q1 & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (32 * (wp * NB + j) < nvalid) {
+#pragma unroll
+                    for (int a = 0; a < NA; ++a)
+                        acc[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[q & 1],
+                                                                          acc[a][j], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (j == NB - 1 && u + 1 < kStage * 4) {
+                    if ((u + 1) / 4 < nsteps)
+                        convert(std::integral_constant<int, (u + 1) / 4>{},
+                                std::integral_constant<int, (u + 1) % 4>{}, af);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (q == 0) {
+                    after_first();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        });
+      }
     };
 
     // prologue: weight scales and stage 0 in LDS, stage 0's and 1's weights
@@ -417,6 +506,25 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     load_a(1, a_ring[1]);
     wait_vm<kALoads>();
     lds_barrier();
+    if constexpr (!kGateUp) {
+        // Down: each A fragment row's largest scale byte bmax; the row's
+        // scale bytes b are rewritten in place as max(0, b - bmax + 140), the
+        // fp32 biased exponent of its conversion scale 2^(b - bmax + 13)
+        // (0: the scale is 0, the codes are more than 139 binades down).
+        // The WP wavefronts of a row group share its copy; wp == 0 rewrites.
+        if (wp == 0) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                uint8_t* run = wave_sc + a * K + n * nblk;
+                int mx = 0;
+                for (int b = g; b < nblk; b += 2) mx = max(mx, (int)run[b]);
+                mx = max(mx, __shfl_xor(mx, 32));
+                for (int b = g; b < nblk; b += 2) run[b] = (uint8_t)max(0, (int)run[b] - mx + 140);
+                if (g == 0) s_rmax[wr][a][n] = mx;
+            }
+        }
+        lds_barrier();
+    }
     // Stage i: products from buffer i % 2 and slot i % 3, with stage i + 1's
     // activations and stage i + 2's weights issued right after the first
     // group of them (buffer (i + 1) % 2 was last read in stage i - 1, slot
@@ -456,50 +564,30 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     wait_vm_all();
 
     if constexpr (kGateUp) {
-        // h = silu(g) * u for features 32 f .. 32 f + 31 (block f of the down
-        // contraction) -> 3 fp8 terms.  Lanes n and n + 32 hold the block's
-        // two halves for pair n.  A wave's two fragments are one 64-feature
-        // step; it assembles its pairs' step chunks in LDS (free now), then
-        // writes them with contiguous 16-byte stores.
-        constexpr int kChunkH = term_chunk(3);
+        // h = silu(g) * u, rounded to fp16, for the wave's two feature
+        // fragments (features 64 sF .. 64 sF + 63, one step of the h rows).
+        // Lanes n and n + 32 hold the features of pair n; the wave assembles
+        // its pairs' 128-byte row pieces in LDS (free now), then writes them
+        // with contiguous 16-byte stores.
+        typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
         constexpr int kWavePairs = 32 * NB;
-        const size_t RBh = (size_t)(F / 64) * kChunkH;
         __syncthreads();                                // every wave is done with the stage buffers
-        uint8_t* wst = lds + wave * (kWavePairs * kChunkH);
+        uint8_t* wst = lds + wave * (kWavePairs * kHPitch);
         if (wcnt > 0) {
             const int sF = wf0 >> 1;
 #pragma unroll
             for (int ff = 0; ff < 2; ++ff) {
-                const int hb = ff;                      // fragment wf0 + ff, wf0 even
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    float h[16];
+                    uint8_t* prow = wst + (32 * j + n) * kHPitch + 64 * ff;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) h[i] = silu_f32(acc[ff][j][i]) * acc[2 + ff][j][i];
-                    uint8_t* chunk = wst + (32 * j + n) * kChunkH;
+                    for (int w = 0; w < 4; ++w) {
+                        // features 32 ff + 8 w + 4 g .. + 3 (C elements 4 w .. 4 w + 3)
+                        f16x4_t hv;
 #pragma unroll
-                    for (int t = 0; t < 3; ++t) {
-                        float amax = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(h[i]));
-                        amax = fmaxf(amax, __shfl_xor(amax, 32));
-                        const int se = fp8_term_exponent(amax);
-                        const float inv = exp2i_neg(se), sc = exp2i(se);
-                        uint32_t q[4];
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            q[w] = pack4_fp8(h[4 * w] * inv, h[4 * w + 1] * inv, h[4 * w + 2] * inv,
-                                             h[4 * w + 3] * inv);
-                        if (t < 2) {
-#pragma unroll
-                            for (int w = 0; w < 4; ++w) sub4_fp8(h + 4 * w, q[w], sc);
-                        }
-                        // elements 8 w + 4 g .. + 3 of the block
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            *reinterpret_cast<uint32_t*>(chunk + t * 64 + (w >> 1) * 32 + 16 * hb +
-                                                         (w & 1) * 8 + 4 * g) = q[w];
-                        if (g == 0) chunk[3 * 64 + 2 * t + hb] = (uint8_t)(se + 127);
+                        for (int c = 0; c < 4; ++c)
+                            hv[c] = (_Float16)(silu_f32(acc[ff][j][4 * w + c]) * acc[2 + ff][j][4 * w + c]);
+                        *reinterpret_cast<f16x4_t*>(prow + 2 * (8 * w + 4 * g)) = hv;
                     }
                 }
             }
@@ -508,12 +596,11 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // pairs wp * kWavePairs .. + kWavePairs - 1 of the tile, step sF
             const int pr0 = wp * kWavePairs;
-            for (int pc = lane; pc < kWavePairs * (kChunkH / 16); pc += 64) {
-                const int pr = pc / (kChunkH / 16), piece = pc - pr * (kChunkH / 16);
+            for (int pc = lane; pc < kWavePairs * 8; pc += 64) {
+                const int pr = pc >> 3, piece = pc & 7;
                 if (pr0 + pr < nvalid)
-                    *reinterpret_cast<u32x4_t*>(hq + (size_t)(row0 + pr0 + pr) * RBh +
-                                                (size_t)sF * kChunkH + 16 * piece) =
-                        *reinterpret_cast<const u32x4_t*>(wst + pr * kChunkH + 16 * piece);
+                    *reinterpret_cast<u32x4_t*>(h + (size_t)(row0 + pr0 + pr) * F + 64 * sF + 8 * piece) =
+                        *reinterpret_cast<const u32x4_t*>(wst + pr * kHPitch + 16 * piece);
             }
         }
     } else {
@@ -521,16 +608,24 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
         for (int a = 0; a < NA; ++a) {
             if (a >= wcnt) break;
             const int f = wf0 + a;
+            // element i (feature row 8 (i / 4) + 4 g + i % 4 of the fragment)
+            // is scaled by 2^(bmax of that row - 140)
+            int ex[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ex[i] = s_rmax[wr][a][8 * (i / 4) + 4 * g + i % 4] - 140;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int r = 32 * (wp * NB + j) + n;
                 if (r < nvalid) {
                     float* orow = y + (size_t)(row0 + r) * NOUT + 32 * f + 4 * g;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        *reinterpret_cast<f32x4_t*>(orow + 8 * w) =
-                            f32x4_t{acc[a][j][4 * w], acc[a][j][4 * w + 1], acc[a][j][4 * w + 2],
-                                    acc[a][j][4 * w + 3]};
+                    for (int w = 0; w < 4; ++w) {
+                        f32x4_t o;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            o[c] = __builtin_amdgcn_ldexpf(acc[a][j][4 * w + c], ex[4 * w + c]);
+                        *reinterpret_cast<f32x4_t*>(orow + 8 * w) = o;
+                    }
                 }
             }
         }
@@ -563,19 +658,20 @@ static int gemm_col_tiles(int NOUT, int frags_per_block) {
 
 // Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps
 // plus 4 waves x 4 fragments of weight scales (K bytes each).
-size_t gemm_lds_bytes(int K, int NT, int stage, int wr) {
-    return (size_t)2 * stage * kGemmRows * term_chunk(NT) + (size_t)4 * wr * K + 8 * 1024;
+size_t gemm_lds_bytes(int K, bool gate_up, int stage, int wr) {
+    const int pitch = gate_up ? term_chunk(2) : kHPitch;
+    return (size_t)2 * stage * kGemmRows * pitch + (size_t)4 * wr * K + 8 * 1024;
 }
 
 
 template <bool kGateUp, int kStage, int WR, int WP, bool kPacked>
 static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t* sorted,
                               const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
-                              int K, int NOUT, uint8_t* hq, float* y, hipStream_t stream) {
+                              int K, int NOUT, _Float16* h, float* y, hipStream_t stream) {
     const int ntl = gemm_col_tiles(NOUT, WR * (kGateUp ? 2 : 4));
-    size_t lds = gemm_lds_bytes(K, kGateUp ? 2 : 3, kStage, WR);
-    if (kGateUp)                                        // epilogue staging of the h term rows
-        lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * term_chunk(3));
+    size_t lds = gemm_lds_bytes(K, kGateUp, kStage, WR);
+    if (kGateUp)                                        // epilogue staging of the h rows
+        lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * kHPitch);
     if (lds > 65536) {
         const hipError_t er = hipFuncSetAttribute(
             reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage, WR, WP, kPacked>),
@@ -585,7 +681,7 @@ static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t
     hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, kStage, WR, WP, kPacked>),
                        dim3((unsigned)gemm_grid(p.max_tiles, ntl)), dim3(64 * WR * WP), lds,
                        stream, bq, sorted, p.k, wq, ws, tiles, p.max_tiles, ntl, K, NOUT, p.F,
-                       hq, y);
+                       h, y);
     return hipSuccess;
 }
 
@@ -595,7 +691,7 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
                            const int32_t* offsets, const int32_t* sorted, float* y, char* base,
                            hipEvent_t* events, hipStream_t stream) {
     uint8_t* xq = reinterpret_cast<uint8_t*>(base + p.off_xq);
-    uint8_t* hq = reinterpret_cast<uint8_t*>(base + p.off_hq);
+    _Float16* h = reinterpret_cast<_Float16*>(base + p.off_h);
     int32_t* tiles = reinterpret_cast<int32_t*>(base + p.off_tiles);
     hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(256), 0, stream, offsets, p.E,
                        p.max_tiles, tiles);
@@ -607,18 +703,19 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
         if (er != hipSuccess) return er;
     }
     hipError_t er;
-    er = packed ? launch_gemm<true, 1, 2, 2, true>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq,
+    er = packed ? launch_gemm<true, 1, 2, 2, true>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, h,
                                                    nullptr, stream)
-                : launch_gemm<true, 1, 2, 2, false>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, hq,
+                : launch_gemm<true, 1, 2, 2, false>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, h,
                                                     nullptr, stream);
     if (er != hipSuccess) return er;
     if (events) {
         er = hipEventRecord(events[1], stream);
         if (er != hipSuccess) return er;
     }
-    er = packed ? launch_gemm<false, 1, 4, 2, true>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D,
+    const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
+    er = packed ? launch_gemm<false, 1, 4, 2, true>(p, hb, nullptr, w2q, w2s, tiles, p.F, p.D,
                                                     nullptr, y, stream)
-                : launch_gemm<false, 1, 4, 2, false>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D,
+                : launch_gemm<false, 1, 4, 2, false>(p, hb, nullptr, w2q, w2s, tiles, p.F, p.D,
                                                      nullptr, y, stream);
     if (er != hipSuccess) return er;
     return hipGetLastError();

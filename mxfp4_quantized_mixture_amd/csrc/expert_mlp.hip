@@ -666,9 +666,9 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     // (the grouped GEMM addresses its buffers with 32-bit byte offsets)
     const size_t k4G = (size_t)1 << 32;
     p.gemm_ok = D % 64 == 0 && F % 64 == 0 && D <= kGemmMaxContraction &&
-                F <= kGemmMaxContraction && gemm_lds_bytes(D, 2, 1, 4) <= kGemmMaxLds &&
-                gemm_lds_bytes(F, 3, 1, 4) <= kGemmMaxLds && gemm_term_bytes(T, D, 2) < k4G &&
-                gemm_term_bytes((int)P, F, 3) < k4G && (size_t)E * F * D < k4G;
+                F <= kGemmMaxContraction && gemm_lds_bytes(D, true, 1, 4) <= kGemmMaxLds &&
+                gemm_lds_bytes(F, false, 1, 4) <= kGemmMaxLds && gemm_term_bytes(T, D, 2) < k4G &&
+                P * F * sizeof(_Float16) < k4G && (size_t)E * F * D < k4G;
     // Weight streaming reads every touched expert's weights once per 16 of its
     // pairs; the grouped GEMM stages 128-pair tiles.  Switch once the average
     // expert receives 32 pairs.
@@ -679,16 +679,15 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     p.max_tiles = gemm_max_tiles(T, E, k);
     p.off_y = 0;
     const size_t scratch = align256(P * D * sizeof(float));
-    p.off_h = scratch;
-    const size_t stream_end = align256(p.off_h + P * F * sizeof(_Float16));
-    size_t gemm_end = scratch;
+    p.off_h = scratch;                         // h [P, F] fp16, both algorithms
+    const size_t h_end = align256(p.off_h + P * F * sizeof(_Float16));
+    size_t gemm_end = h_end;
     if (p.gemm_ok) {
-        p.off_xq = scratch;
-        p.off_hq = align256(p.off_xq + gemm_term_bytes(T, D, 2));
-        p.off_tiles = align256(p.off_hq + gemm_term_bytes((int)P, F, 3));
+        p.off_xq = h_end;
+        p.off_tiles = align256(p.off_xq + gemm_term_bytes(T, D, 2));
         gemm_end = align256(p.off_tiles + sizeof(int32_t) * (2 * (size_t)p.max_tiles + 1));
     }
-    p.ws_bytes = std::max(stream_end, gemm_end);
+    p.ws_bytes = gemm_end;
     return p;
 }
 

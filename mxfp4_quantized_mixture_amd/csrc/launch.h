@@ -38,8 +38,8 @@ struct MlpPlan {
     bool packed_ok;      // packed weights accepted: both algorithms take the shape
     int max_tiles;       // upper bound of 128-pair tiles over all experts
     size_t off_y;
-    size_t off_h;                                    // streaming: h fp16 [P, F]
-    size_t off_xq, off_hq, off_tiles;              // grouped GEMM
+    size_t off_h;                                    // h fp16 [P, F]
+    size_t off_xq, off_tiles;                        // grouped GEMM: x terms, tile table
     size_t ws_bytes;
 };
 MlpPlan plan_mlp(int T, int D, int F, int E, int k);
@@ -54,8 +54,8 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
 // grouped-GEMM path (expert_gemm.hip)
 int gemm_max_tiles(int T, int E, int k);
 size_t gemm_term_bytes(int rows, int K, int NT);
-size_t gemm_lds_bytes(int K, int NT, int stage, int wr);
-constexpr size_t kGemmMaxLds = 159 * 1024;    // of 160 KiB; the rest is static LDS
+size_t gemm_lds_bytes(int K, bool gate_up, int stage, int wr);
+constexpr size_t kGemmMaxLds = 157 * 1024;    // of 160 KiB; the rest is static LDS
 constexpr int kGemmMaxContraction = 8192;      // D and F limit of the grouped GEMM
 hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,

@@ -384,6 +384,35 @@ def test_layer_grouped_gemm_shapes(cfg):
     check_layer(Inputs(cfg, 4), what=cfg.name + "/grouped-gemm", algo=moe.MLP_GROUPED_GEMM)
 
 
+class W2ScaledInputs(Inputs):
+    """Inputs whose W2 blocks are multiplied by powers of two (exact in
+    bf16): "spread" draws a factor 2^(30 - r), r in [0, 40], per 32-element
+    block, block 0 of every row taking 2^30 (so each row's blocks reach 40
+    binades below its largest, and every row has the same top scale);
+    "large" multiplies every W2 weight by 2^40, "small" by 2^-90.  The down
+    contraction's block scales then leave fp16's range."""
+
+    def __init__(self, cfg, seed, mode):
+        super().__init__(cfg, seed)
+        rng = np.random.default_rng(seed + 1000)
+        w2 = MI.bf16_bits_to_f32(self.w2).reshape(cfg.E, cfg.D, cfg.F // 32, 32)
+        if mode == "spread":
+            r = 30.0 - rng.integers(0, 41, size=w2.shape[:3]).astype(np.float32)
+            r[:, :, 0] = 30.0
+        else:
+            r = np.full(w2.shape[:3], 40.0 if mode == "large" else -90.0, np.float32)
+        w2 = w2 * np.exp2(r)[..., None]
+        self.w2 = MI.f32_to_bf16_bits(w2.reshape(cfg.E, cfg.D, cfg.F))
+
+
+@pytest.mark.parametrize("mode", ["spread", "large", "small"])
+@pytest.mark.parametrize("algo", [moe.MLP_GROUPED_GEMM, moe.MLP_STREAM])
+def test_layer_w2_block_scales_outside_fp16_range(mode, algo):
+    cfg = MI.MoEConfig("w2_scales", T=300, D=192, F=320, E=4, k=2)
+    check_layer(W2ScaledInputs(cfg, 6, mode), what="w2 scales %s/algo %d" % (mode, algo),
+                algo=algo)
+
+
 @pytest.mark.parametrize("name", ["gemm_skewed", "gemm_full_width"])
 def test_layer_streaming_on_gemm_shapes(name):
     cfg = {c.name: c for c in GEMM_EDGE}[name]
