@@ -184,17 +184,19 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM.  Block = one tile of kGemmRows pairs x one column range of
-// output fragments (32 outputs each).  Four wavefronts in WR row groups x
-// 4 / WR pair groups; each owns 128 / (4 / WR) pairs (NB B fragments) and
-// kWaveFrags output fragments (WR = 4: one block per CU with 128 x 128
-// accumulator tiles; WR = 2: two blocks per CU with 128 x 64 tiles):
-//   gate/up: 2 feature fragments -> 4 A fragments (their gate and up rows),
-//            epilogue h = silu(g) * u written as fp16 rows;
-//   down:    4 output fragments -> 4 A fragments, epilogue y (fp32).
-// The contraction runs in stages of kStage 64-wide steps (128 per stage
-// when LDS allows): activations go global -> registers -> one of two LDS
-// buffers, weights global -> registers, each a stage ahead, with one
-// barrier per stage.
+// output fragments (32 outputs each).  WR row groups x WP pair groups of
+// wavefronts; each owns 128 / WP pairs (NB = 4 / WP B fragments) and
+// kWaveFrags output fragments:
+//   gate/up (2 x 2, two blocks per CU): 2 feature fragments -> 4 A
+//            fragments (their gate and up rows), epilogue h = silu(g) * u
+//            written as fp16 rows;
+//   down (8 x 1, one block per CU): 2 output fragments -> 2 A fragments,
+//            each converted code serving the wave's 4 pair fragments (the
+//            conversions do not overlap the products, so their number per
+//            product matters), epilogue y (fp32).
+// The contraction runs in stages of kStage 64-wide steps: activations go
+// global -> LDS by direct loads one stage ahead, weights global ->
+// registers two stages ahead, with one barrier per stage.
 // ---------------------------------------------------------------------------
 // kPacked: wq in the mxfp4_pack layout (a fragment's 32 rows x 32 bytes of
 // one step are a contiguous 1 KiB chunk: 16-byte piece 32 h + r holds half h
@@ -207,11 +209,13 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
     _Float16* __restrict__ h, float* __restrict__ y) {
     constexpr int NT = 2;                               // x terms (gate/up)
-    constexpr int NA = 4;                               // A fragments per wave
+    // A fragments per wave: gate/up 4 (the gate and up rows of 2 feature
+    // fragments), down 16 / WR (a block covers 16 output fragments)
+    constexpr int NA = kGateUp ? 4 : 16 / WR;
     constexpr int kGemmThreads = 64 * WR * WP;
     constexpr int NB = 4 / WP;                          // B fragments (32 pairs) per wave
-    static_assert(WR <= 4 && WR * WP <= 8, "wavefront layout");
-    constexpr int kWaveFrags = kGateUp ? 2 : 4;         // output fragments per wave
+    static_assert(WR * WP <= 8 && (kGateUp ? WR <= 4 : 16 % WR == 0), "wavefront layout");
+    constexpr int kWaveFrags = kGateUp ? 2 : NA;        // output fragments per wave
     // A step of an activation row: kStepBytes in global memory (x: the
     // terms and scales of one step chunk; h: 64 fp16 values), kChunk in LDS
     // (h: plus a pad unit, loaded as a copy of the step's last 16 bytes).
@@ -225,9 +229,14 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     constexpr int kRowPieces = kChunk / 16;
     constexpr int kPieces = (kGemmRows * kRowPieces + kGemmThreads - 1) / kGemmThreads;
     constexpr int kBufBytes = kStage * kSlotBytes;      // one stage of activation steps
+    // Activation loads run one stage ahead through two LDS buffers.  (Two
+    // stages ahead gains nothing: the compiler's own wait for the weight
+    // registers at the start of a stage does not count the direct-to-LDS
+    // loads, which are opaque to it, and so also drains the newer ones.)
+    constexpr int kBufs = 2;
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int s_src[kGemmRows];
-    __shared__ int s_rmax[4][NA][32];                   // (down) bmax of each A fragment row
+    __shared__ int s_rmax[WR][NA][32];                  // (down) bmax of each A fragment row
 
     // Work item L = m-tile * ntl + column tile.  The dispatcher deals blocks
     // to the 8 XCDs round robin (block b -> XCD b % 8), each XCD with its own
@@ -242,7 +251,10 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     const int mt = L / ntl, nt = L - mt * ntl;
     const int row0 = tiles[2 * mt], info = tiles[2 * mt + 1];
     const int e = info & 0xFFFF, nvalid = info >> 16;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index through readfirstlane: the compiler then knows it is
+    // uniform, keeps what derives from it in scalar registers and branches
+    // on it with scalar branches)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / WP, wp = wave % WP;           // this wave's row group and pair group
     const int n = lane & 31, g = lane >> 5;
     const int S = K / 64;
@@ -269,7 +281,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     // 16-byte aligned run of 32 * nblk = K bytes; each wave copies its
     // fragments' runs into its own LDS area once.
     // (the WP wavefronts of a row group share one copy, made by wp == 0)
-    uint8_t* wave_sc = lds + 2 * kBufBytes + (size_t)wr * NA * K;
+    uint8_t* wave_sc = lds + kBufs * kBufBytes + (size_t)wr * NA * K;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
         const int slot = kGateUp ? (a & 1) : a;         // gate/up: a = 0, 1 gate; 2, 3 up
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     };
     // this lane's scale bytes: row n of each fragment, block 2 s + g at + 2 s
     const uint8_t* my_sc = wave_sc + n * nblk + g;
-    uint8_t* dummy = lds + 2 * kBufBytes + (size_t)WR * NA * K + (wave & 7) * 1024;
+    uint8_t* dummy = lds + kBufs * kBufBytes + (size_t)WR * NA * K + (wave & 7) * 1024;
     __syncthreads();
 
     // Staging: piece p = tid + 256 c (p < 128 kRowPieces) is 16-byte piece
@@ -432,21 +444,20 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
             }
         });
       } else {
-        // Group q = (step kk, sub-step jj, pair fragment j): the NA products
-        // over elements 8 jj .. 8 jj + 7 of each lane's 32.  The A fragments
-        // of sub-step jj + 1 are converted once sub-step jj's last products
-        // are issued (they run meanwhile), and group q + 1's h operand is
-        // read from LDS during group q.
-        constexpr int kGroups = kStage * 4 * NB;
+        // Sub-step u = (step kk, jj): the NA x NB products over elements
+        // 8 jj .. 8 jj + 7 of each lane's 32.  Sub-step u + 1's h operands
+        // (all NB pair fragments) are read from LDS and its A fragments
+        // converted while sub-step u's products run.
+        constexpr int kSub = kStage * 4;
         float sc[kStage][NA];                           // conversion scales (rewritten bytes)
 #pragma unroll
         for (int kk = 0; kk < kStage; ++kk)
 #pragma unroll
             for (int a = 0; a < NA; ++a)
                 sc[kk][a] = __builtin_bit_cast(float, (uint32_t)my_sc[a * K + 2 * min(s0 + kk, S - 1)] << 23);
-        f16x8_t af[NA], bf[2];
-        auto convert = [&](auto kc, auto jc, f16x8_t(&dst)[NA]) {
-            constexpr int kk = decltype(kc)::value, jj = decltype(jc)::value;
+        f16x8_t af[2][NA], bf[2][NB];
+        auto convert = [&](auto uc, f16x8_t(&dst)[NA]) {
+            constexpr int kk = decltype(uc)::value / 4, jj = decltype(uc)::value % 4;
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
                 const uint32_t w = a_cur[kk][a][jj];
@@ -459,36 +470,39 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
                 dst[a] = __builtin_bit_cast(f16x8_t, v);
             }
         };
-        auto read_b = [&](int kk, int j, int jj, f16x8_t& dst) {
-            // pair 32 j + n of the step: elements 32 g + 8 jj .. + 7
-            const uint8_t* row = lds + buf * kBufBytes + kk * kSlotBytes + (32 * (wp * NB + j) + n) * kChunk;
-            dst = *reinterpret_cast<const f16x8_t*>(row + 64 * g + 16 * jj);
-        };
-        convert(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, af);
-        read_b(0, 0, 0, bf[0]);
-        static_for<kGroups>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            constexpr int u = q / NB, kk = u / 4, j = q % NB;
-            if (kk < nsteps) {
-                if constexpr (q + 1 < kGroups) {
-                    constexpr int q1 = q + 1;
-                    if (q1 / (4 * NB) < nsteps) read_b(q1 / (4 * NB), q1 % NB, (q1 / NB) % 4, bf[q1 & 1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (32 * (wp * NB + j) < nvalid) {
+        auto read_b = [&](int u, f16x8_t(&dst)[NB]) {
+            // pair 32 (wp NB + j) + n of step u / 4: elements 32 g + 8 (u % 4) .. + 7
 #pragma unroll
-                    for (int a = 0; a < NA; ++a)
-                        acc[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[q & 1],
-                                                                          acc[a][j], 0, 0, 0);
+            for (int j = 0; j < NB; ++j) {
+                const uint8_t* row = lds + buf * kBufBytes + (u / 4) * kSlotBytes +
+                                     (32 * (wp * NB + j) + n) * kChunk;
+                dst[j] = *reinterpret_cast<const f16x8_t*>(row + 64 * g + 16 * (u % 4));
+            }
+        };
+        convert(std::integral_constant<int, 0>{}, af[0]);
+        read_b(0, bf[0]);
+        static_for<kSub>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            if (u / 4 < nsteps) {
+                if constexpr (u + 1 < kSub) {
+                    if ((u + 1) / 4 < nsteps) {
+                        read_b(u + 1, bf[(u + 1) & 1]);
+                        convert(std::integral_constant<int, u + 1>{}, af[(u + 1) & 1]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (j == NB - 1 && u + 1 < kStage * 4) {
-                    if ((u + 1) / 4 < nsteps)
-                        convert(std::integral_constant<int, (u + 1) / 4>{},
-                                std::integral_constant<int, (u + 1) % 4>{}, af);
-                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    // (pair fragments past the tile's pairs: no products)
+                    if (32 * (wp * NB + j) < nvalid) {
+#pragma unroll
+                        for (int a = 0; a < NA; ++a)
+                            acc[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                af[u & 1][a], bf[u & 1][j], acc[a][j], 0, 0, 0);
+                    }
                 }
-                if constexpr (q == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (u == 0) {
                     after_first();
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -532,23 +546,34 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     // weights in flight: activations get almost one stage to land, weights
     // almost two.  The loop takes three stages per trip, without branches,
     // so that every register slot keeps one fixed set of registers.
-    auto run_stage = [&](int i, auto rc) {
+    //
+    // The count in wait_vm<kALoads> holds only where the weight loads of
+    // the stage are live.  After the loop they are not (no later stage reads
+    // them), the compiler drops them, and the count would then leave
+    // activation loads in flight; the (at most two) stages after the loop
+    // therefore wait for everything.
+    auto run_stage = [&](int i, auto rc, auto tail) {
         constexpr int r = decltype(rc)::value;
         compute_stage(i & 1, i * kStage, kStage, a_ring[r], [&]() {
             load_act(i + 1);
             load_a(i + 2, a_ring[(r + 2) % 3]);
         });
-        wait_vm<kALoads>();
+        if constexpr (decltype(tail)::value)
+            wait_vm_all();
+        else
+            wait_vm<kALoads>();
         lds_barrier();
     };
+    using Loop = std::false_type;
+    using Tail = std::true_type;
     int i0 = 0;
     for (; i0 + 3 <= nst; i0 += 3) {
-        run_stage(i0, std::integral_constant<int, 0>{});
-        run_stage(i0 + 1, std::integral_constant<int, 1>{});
-        run_stage(i0 + 2, std::integral_constant<int, 2>{});
+        run_stage(i0, std::integral_constant<int, 0>{}, Loop{});
+        run_stage(i0 + 1, std::integral_constant<int, 1>{}, Loop{});
+        run_stage(i0 + 2, std::integral_constant<int, 2>{}, Loop{});
     }
-    if (i0 < nst) run_stage(i0, std::integral_constant<int, 0>{});
-    if (i0 + 1 < nst) run_stage(i0 + 1, std::integral_constant<int, 1>{});
+    if (i0 < nst) run_stage(i0, std::integral_constant<int, 0>{}, Tail{});
+    if (i0 + 1 < nst) run_stage(i0 + 1, std::integral_constant<int, 1>{}, Tail{});
     if constexpr (kStage > 1) {
         if (nst * kStage < S) {                         // partial last stage, slot nst % 3
             const int s0 = nst * kStage, ns = S - s0;
@@ -656,11 +681,13 @@ static int gemm_col_tiles(int NOUT, int frags_per_block) {
     return (NOUT / 32 + frags_per_block - 1) / frags_per_block;
 }
 
-// Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps
-// plus 4 waves x 4 fragments of weight scales (K bytes each).
+// Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps,
+// the weight scales of the block's A fragments (K bytes each; gate/up 4 per
+// row group, down 16), and 8 KiB of dummy destinations for the staging.
 size_t gemm_lds_bytes(int K, bool gate_up, int stage, int wr) {
     const int pitch = gate_up ? term_chunk(2) : kHPitch;
-    return (size_t)2 * stage * kGemmRows * pitch + (size_t)4 * wr * K + 8 * 1024;
+    const int frags = gate_up ? 4 * wr : 16;           // A fragments per block
+    return (size_t)2 * stage * kGemmRows * pitch + (size_t)frags * K + 8 * 1024;
 }
 
 
@@ -668,7 +695,7 @@ template <bool kGateUp, int kStage, int WR, int WP, bool kPacked>
 static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t* sorted,
                               const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
                               int K, int NOUT, _Float16* h, float* y, hipStream_t stream) {
-    const int ntl = gemm_col_tiles(NOUT, WR * (kGateUp ? 2 : 4));
+    const int ntl = gemm_col_tiles(NOUT, kGateUp ? 2 * WR : 16);
     size_t lds = gemm_lds_bytes(K, kGateUp, kStage, WR);
     if (kGateUp)                                        // epilogue staging of the h rows
         lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * kHPitch);
@@ -713,9 +740,9 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
         if (er != hipSuccess) return er;
     }
     const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
-    er = packed ? launch_gemm<false, 1, 4, 2, true>(p, hb, nullptr, w2q, w2s, tiles, p.F, p.D,
+    er = packed ? launch_gemm<false, 1, 8, 1, true>(p, hb, nullptr, w2q, w2s, tiles, p.F, p.D,
                                                     nullptr, y, stream)
-                : launch_gemm<false, 1, 4, 2, false>(p, hb, nullptr, w2q, w2s, tiles, p.F, p.D,
+                : launch_gemm<false, 1, 8, 1, false>(p, hb, nullptr, w2q, w2s, tiles, p.F, p.D,
                                                      nullptr, y, stream);
     if (er != hipSuccess) return er;
     return hipGetLastError();
