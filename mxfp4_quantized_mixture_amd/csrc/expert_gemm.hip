@@ -187,8 +187,9 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 // output fragments (32 outputs each).  WR row groups x WP pair groups of
 // wavefronts; each owns 128 / WP pairs (NB = 4 / WP B fragments) and
 // kWaveFrags output fragments:
-//   gate/up (2 x 2, two blocks per CU): 2 feature fragments -> 4 A
-//            fragments (their gate and up rows), epilogue h = silu(g) * u
+//   gate/up (4 x 1, two blocks per CU): 1 feature fragment -> 2 A
+//            fragments (its gate and up rows) x all 4 pair fragments (no
+//            two wavefronts load the same weights), epilogue h = silu(g) * u
 //            written as fp16 rows;
 //   down (8 x 1, one block per CU): 2 output fragments -> 2 A fragments,
 //            each converted code serving the wave's 4 pair fragments (the
@@ -209,13 +210,13 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
     _Float16* __restrict__ h, float* __restrict__ y) {
     constexpr int NT = 2;                               // x terms (gate/up)
-    // A fragments per wave: gate/up 4 (the gate and up rows of 2 feature
-    // fragments), down 16 / WR (a block covers 16 output fragments)
-    constexpr int NA = kGateUp ? 4 : 16 / WR;
+    // A fragments per wave: gate/up the gate and up rows of 4 / WR feature
+    // fragments (a block covers 4), down 16 / WR (a block covers 16)
+    constexpr int NA = kGateUp ? 8 / WR : 16 / WR;
     constexpr int kGemmThreads = 64 * WR * WP;
     constexpr int NB = 4 / WP;                          // B fragments (32 pairs) per wave
-    static_assert(WR * WP <= 8 && (kGateUp ? WR <= 4 : 16 % WR == 0), "wavefront layout");
-    constexpr int kWaveFrags = kGateUp ? 2 : NA;        // output fragments per wave
+    static_assert(WR * WP <= 8 && (kGateUp ? 4 % WR == 0 : 16 % WR == 0), "wavefront layout");
+    constexpr int kWaveFrags = kGateUp ? NA / 2 : NA;   // output fragments per wave
     // A step of an activation row: kStepBytes in global memory (x: the
     // terms and scales of one step chunk; h: 64 fp16 values), kChunk in LDS
     // (h: plus a pad unit, loaded as a copy of the step's last 16 bytes).
@@ -268,10 +269,10 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
 
     // This block's output fragments [fa, fb); this wave's [wf0, wf0 + wcnt).
     const int nfrag = NOUT / 32;
-    // (gate/up: whole 64-feature steps per block, so each wave's two feature
-    // fragments form one step of the h term rows; down: an even split)
-    const int fa = kGateUp ? nt * 2 * WR : (int)((int64_t)nfrag * nt / ntl);
-    const int fb = kGateUp ? min(fa + 2 * WR, nfrag) : (int)((int64_t)nfrag * (nt + 1) / ntl);
+    // (gate/up: 4 fragments, two whole 64-feature steps of h, per block;
+    // down: an even split)
+    const int fa = kGateUp ? nt * 4 : (int)((int64_t)nfrag * nt / ntl);
+    const int fb = kGateUp ? min(fa + 4, nfrag) : (int)((int64_t)nfrag * (nt + 1) / ntl);
     const int wf0 = fa + wr * kWaveFrags;
     const int wcnt = max(0, min(kWaveFrags, fb - wf0));
     const int R = kGateUp ? 2 * F : NOUT;               // weight rows per expert
@@ -284,9 +285,10 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     uint8_t* wave_sc = lds + kBufs * kBufBytes + (size_t)wr * NA * K;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
-        const int slot = kGateUp ? (a & 1) : a;         // gate/up: a = 0, 1 gate; 2, 3 up
+        // gate/up: a < kWaveFrags the gate rows of fragment wf0 + a, then the up rows
+        const int slot = kGateUp ? a % kWaveFrags : a;
         const int f = slot < wcnt ? wf0 + slot : fa;    // idle fragments recompute fragment fa
-        const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
+        const int frow = (kGateUp && a >= kWaveFrags ? F : 0) + 32 * f;
         // (the fragment's first byte is the same in both layouts)
         aoff[a] = kPacked ? (uint32_t)(((size_t)e * R + frow) * (size_t)(K / 2) + 16 * lane)
                           : (uint32_t)(((size_t)e * R + frow + n) * (size_t)(K / 2) + 16 * g);
@@ -298,9 +300,9 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
         if (wp != 0) return;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-            const int slot = kGateUp ? (a & 1) : a;
+            const int slot = kGateUp ? a % kWaveFrags : a;
             const int f = slot < wcnt ? wf0 + slot : fa;
-            const int frow = (kGateUp && a >= 2 ? F : 0) + 32 * f;
+            const int frow = (kGateUp && a >= kWaveFrags ? F : 0) + 32 * f;
             const uint8_t* run = wsc + ((size_t)e * R + frow) * nblk;
 #pragma unroll
             for (int it = 0; it < kScaleIters; ++it) {
@@ -589,29 +591,31 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     wait_vm_all();
 
     if constexpr (kGateUp) {
-        // h = silu(g) * u, rounded to fp16, for the wave's two feature
-        // fragments (features 64 sF .. 64 sF + 63, one step of the h rows).
-        // Lanes n and n + 32 hold the features of pair n; the wave assembles
-        // its pairs' 128-byte row pieces in LDS (free now), then writes them
-        // with contiguous 16-byte stores.
+        // h = silu(g) * u, rounded to fp16, for the wave's kWaveFrags feature
+        // fragments (features 32 wf0 .. 32 (wf0 + kWaveFrags) - 1).  Lanes n
+        // and n + 32 hold the features of pair n; the wave assembles its
+        // pairs' 64 kWaveFrags-byte row pieces in LDS (free now), then writes
+        // them with contiguous 16-byte stores.
         typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
         constexpr int kWavePairs = 32 * NB;
+        constexpr int kRowPieces16 = 4 * kWaveFrags;    // 16-byte pieces of a row piece
+        constexpr int kRowPitch = 16 * (kRowPieces16 + 1);
         __syncthreads();                                // every wave is done with the stage buffers
-        uint8_t* wst = lds + wave * (kWavePairs * kHPitch);
+        uint8_t* wst = lds + wave * (kWavePairs * kRowPitch);
         if (wcnt > 0) {
-            const int sF = wf0 >> 1;
 #pragma unroll
-            for (int ff = 0; ff < 2; ++ff) {
+            for (int ff = 0; ff < kWaveFrags; ++ff) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    uint8_t* prow = wst + (32 * j + n) * kHPitch + 64 * ff;
+                    uint8_t* prow = wst + (32 * j + n) * kRowPitch + 64 * ff;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         // features 32 ff + 8 w + 4 g .. + 3 (C elements 4 w .. 4 w + 3)
                         f16x4_t hv;
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
-                            hv[c] = (_Float16)(silu_f32(acc[ff][j][4 * w + c]) * acc[2 + ff][j][4 * w + c]);
+                            hv[c] = (_Float16)(silu_f32(acc[ff][j][4 * w + c]) *
+                                               acc[kWaveFrags + ff][j][4 * w + c]);
                         *reinterpret_cast<f16x4_t*>(prow + 2 * (8 * w + 4 * g)) = hv;
                     }
                 }
@@ -619,13 +623,13 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // pairs wp * kWavePairs .. + kWavePairs - 1 of the tile, step sF
+            // pairs wp * kWavePairs .. + kWavePairs - 1 of the tile
             const int pr0 = wp * kWavePairs;
-            for (int pc = lane; pc < kWavePairs * 8; pc += 64) {
-                const int pr = pc >> 3, piece = pc & 7;
+            for (int pc = lane; pc < kWavePairs * kRowPieces16; pc += 64) {
+                const int pr = pc / kRowPieces16, piece = pc % kRowPieces16;
                 if (pr0 + pr < nvalid)
-                    *reinterpret_cast<u32x4_t*>(h + (size_t)(row0 + pr0 + pr) * F + 64 * sF + 8 * piece) =
-                        *reinterpret_cast<const u32x4_t*>(wst + pr * kHPitch + 16 * piece);
+                    *reinterpret_cast<u32x4_t*>(h + (size_t)(row0 + pr0 + pr) * F + 32 * wf0 + 8 * piece) =
+                        *reinterpret_cast<const u32x4_t*>(wst + pr * kRowPitch + 16 * piece);
             }
         }
     } else {
@@ -682,11 +686,11 @@ static int gemm_col_tiles(int NOUT, int frags_per_block) {
 }
 
 // Dynamic LDS of expert_gemm_kernel: two stage buffers of activation steps,
-// the weight scales of the block's A fragments (K bytes each; gate/up 4 per
-// row group, down 16), and 8 KiB of dummy destinations for the staging.
+// the weight scales of the block's A fragments (K bytes each; gate/up 8,
+// down 16), and 8 KiB of dummy destinations for the staging.
 size_t gemm_lds_bytes(int K, bool gate_up, int stage, int wr) {
     const int pitch = gate_up ? term_chunk(2) : kHPitch;
-    const int frags = gate_up ? 4 * wr : 16;           // A fragments per block
+    const int frags = gate_up ? 8 : 16;                 // A fragments per block
     return (size_t)2 * stage * kGemmRows * pitch + (size_t)frags * K + 8 * 1024;
 }
 
@@ -695,10 +699,10 @@ template <bool kGateUp, int kStage, int WR, int WP, bool kPacked>
 static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t* sorted,
                               const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
                               int K, int NOUT, _Float16* h, float* y, hipStream_t stream) {
-    const int ntl = gemm_col_tiles(NOUT, kGateUp ? 2 * WR : 16);
+    const int ntl = gemm_col_tiles(NOUT, kGateUp ? 4 : 16);
     size_t lds = gemm_lds_bytes(K, kGateUp, kStage, WR);
     if (kGateUp)                                        // epilogue staging of the h rows
-        lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * kHPitch);
+        lds = std::max(lds, (size_t)(WR * WP) * 32 * (4 / WP) * 16 * (4 * (4 / WR) + 1));
     if (lds > 65536) {
         const hipError_t er = hipFuncSetAttribute(
             reinterpret_cast<const void*>(&expert_gemm_kernel<kGateUp, kStage, WR, WP, kPacked>),
@@ -730,9 +734,9 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
         if (er != hipSuccess) return er;
     }
     hipError_t er;
-    er = packed ? launch_gemm<true, 1, 2, 2, true>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, h,
+    er = packed ? launch_gemm<true, 1, 4, 1, true>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, h,
                                                    nullptr, stream)
-                : launch_gemm<true, 1, 2, 2, false>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, h,
+                : launch_gemm<true, 1, 4, 1, false>(p, xq, sorted, w13q, w13s, tiles, p.D, p.F, h,
                                                     nullptr, stream);
     if (er != hipSuccess) return er;
     if (events) {
