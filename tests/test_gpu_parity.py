@@ -432,6 +432,34 @@ def test_grouped_gemm_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# Contractions whose 64-wide step count leaves one or two stages after the
+# grouped GEMM's three-stage loop (D/64 = 2 and 5, F/64 = 2 and 5), run
+# repeatedly on workspaces pre-filled with NaN bytes or zeros: the h rows,
+# y and the output must be the same every time (a stage that let its
+# activation loads land after the barrier changed some h rows from run to
+# run).
+@pytest.mark.parametrize("D,F", [(128, 128), (320, 320), (128, 320)])
+def test_grouped_gemm_tail_stages_repeatable(D, F):
+    cfg = MI.MoEConfig("gemm_tail_%dx%d" % (D, F), T=1000, D=D, F=F, E=2, k=2)
+    inp = Inputs(cfg, 9)
+    xd = G.bf16_dev(inp.x)
+    weights = moe.ExpertWeights.quantize(G.bf16_dev(inp.w13), G.bf16_dev(inp.w2))
+    r = moe.moe_route(xd, G.f32_dev(inp.wr), G.f32_dev(inp.b), cfg.k)
+    outs, wss = [], []
+    for rep in range(6):
+        ws = moe.mlp_workspace(cfg.T, D, F, cfg.E, cfg.k, xd.device)
+        ws.fill_(0xFF if rep % 2 == 0 else 0)
+        outs.append(moe.moe_expert_mlp(xd, weights, r, ws=ws, algo=moe.MLP_GROUPED_GEMM))
+        wss.append(ws)
+    torch.cuda.synchronize()
+    P = cfg.T * cfg.k
+    n = (P * D * 4 + 255) // 256 * 256 + P * F * 2          # y, then h
+    for rep in range(1, 6):
+        assert torch.equal(outs[rep].view(torch.int16), outs[0].view(torch.int16)), rep
+        assert torch.equal(wss[rep][:n], wss[0][:n]), rep
+    check_layer(inp, what=cfg.name + "/grouped-gemm", algo=moe.MLP_GROUPED_GEMM)
+
+
 def test_layer_is_deterministic():
     inp = Inputs(MI.CONFIGS["gptoss20b_decode"], 1)
     _, _, a = run_gpu_layer(inp)
