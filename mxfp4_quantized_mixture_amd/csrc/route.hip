@@ -41,8 +41,8 @@ constexpr int kMaxE = 256;
 // summed through LDS in a fixed order.  Slice s writes its partial tile to
 // P[s]; slice 0 adds the bias.  The top-k kernel sums the S slices in order.
 // A block's NE expert tiles share its activation loads (x is read once per
-// expert tile group, not once per 16 experts); KB K-steps' loads are issued
-// together.
+// expert tile group, not once per 16 experts); the operands of KB K-steps
+// are loaded together, one group of KB steps ahead of their products.
 constexpr int kRouterWaves = 4;
 
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8_t& hi, bf16x8_t& mid,
@@ -68,7 +68,7 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], bf16x8_t& hi, b
     lo = as_bf16x8(l);
 }
 
-template <int TT, int NE, int KB>
+template <int TT, int NE, int KB, bool kPipe>
 __global__ __launch_bounds__(kRouterWaves * 64) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
     float* __restrict__ P, int T, int D, int E, int S) {
@@ -80,57 +80,95 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_logits_kernel(
     const int part = sl * kRouterWaves + wave, parts = S * kRouterWaves;
     const int k_beg = (int)((int64_t)nk * part / parts), k_end = (int)((int64_t)nk * (part + 1) / parts);
     const float* wrow[NE];
-    bool eok[NE];
 #pragma unroll
-    for (int n = 0; n < NE; ++n) {
-        const int e = e0 + 16 * n + m;
-        eok[n] = e < E;
-        wrow[n] = wr + (int64_t)(eok[n] ? e : 0) * D;
-    }
+    for (int n = 0; n < NE; ++n) wrow[n] = wr + (int64_t)min(e0 + 16 * n + m, E - 1) * D;
     f32x4_t acc[NE][TT];
 #pragma unroll
     for (int n = 0; n < NE; ++n)
 #pragma unroll
         for (int u = 0; u < TT; ++u) acc[n][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kk = k_beg; kk < k_end; kk += KB) {
+    // Operands of KB K-steps at a time.  kPipe: loaded one group ahead of
+    // the products (two register sets, fixed by unrolling the loop by two
+    // groups); otherwise each group's loads are issued together and then
+    // used.  Loads are unconditional: steps past the slice, experts past E
+    // and tokens past T load clamped, valid addresses (their products are
+    // skipped or their rows never stored), so the compiler never drains the
+    // queue at a branch.
+    struct Ops {
         float4 wa[KB][NE], wb[KB][NE];
         u32x4_t xv[KB][TT];
+    };
+    auto load = [&](Ops& o, int kk) {
 #pragma unroll
         for (int h = 0; h < KB; ++h) {
-            const int off = (kk + h) * 32 + 8 * g;
-            const bool kok = kk + h < k_end;
+            const int off = min(kk + h, k_end - 1) * 32 + 8 * g;
 #pragma unroll
             for (int n = 0; n < NE; ++n) {
-                wa[h][n] = wb[h][n] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (kok && eok[n]) {
-                    wa[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off);
-                    wb[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off + 4);
-                }
+                o.wa[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off);
+                o.wb[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off + 4);
             }
 #pragma unroll
             for (int u = 0; u < TT; ++u) {
-                const int t = t0 + 16 * u + m;
-                xv[h][u] = u32x4_t{0u, 0u, 0u, 0u};
-                if (kok && t < T) xv[h][u] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * D + off);
+                const int t = min(t0 + 16 * u + m, T - 1);
+                o.xv[h][u] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * D + off);
             }
         }
+    };
+    auto compute = [&](const Ops& o, int kk) {
 #pragma unroll
         for (int h = 0; h < KB; ++h) {
             if (kk + h < k_end) {
 #pragma unroll
                 for (int n = 0; n < NE; ++n) {
-                    const float w[8] = {wa[h][n].x, wa[h][n].y, wa[h][n].z, wa[h][n].w,
-                                        wb[h][n].x, wb[h][n].y, wb[h][n].z, wb[h][n].w};
+                    const float w[8] = {o.wa[h][n].x, o.wa[h][n].y, o.wa[h][n].z, o.wa[h][n].w,
+                                        o.wb[h][n].x, o.wb[h][n].y, o.wb[h][n].z, o.wb[h][n].w};
                     bf16x8_t hi, mid, lo;
                     split3_bf16(w, hi, mid, lo);
 #pragma unroll
                     for (int u = 0; u < TT; ++u) {
-                        const bf16x8_t xb = as_bf16x8(xv[h][u]);
+                        const bf16x8_t xb = as_bf16x8(o.xv[h][u]);
                         acc[n][u] = mfma_bf16(hi, xb, acc[n][u]);
                         acc[n][u] = mfma_bf16(mid, xb, acc[n][u]);
                         acc[n][u] = mfma_bf16(lo, xb, acc[n][u]);
                     }
                 }
+            }
+        }
+    };
+    if (k_beg < k_end) {
+        if constexpr (kPipe) {
+            Ops A, B;
+            load(A, k_beg);
+            for (int kk = k_beg; kk < k_end; kk += 2 * KB) {
+                load(B, kk + KB);
+                compute(A, kk);
+                load(A, kk + 2 * KB);
+                compute(B, kk + KB);
+            }
+        } else {
+            for (int kk = k_beg; kk < k_end; kk += KB) {
+                Ops A;
+                if (kk + KB <= k_end) {
+                    load(A, kk);
+                } else {                                // last group: only the slice's steps
+#pragma unroll
+                    for (int h = 0; h < KB; ++h) {
+                        if (kk + h < k_end) {
+                            const int off = (kk + h) * 32 + 8 * g;
+#pragma unroll
+                            for (int n = 0; n < NE; ++n) {
+                                A.wa[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off);
+                                A.wb[h][n] = *reinterpret_cast<const float4*>(wrow[n] + off + 4);
+                            }
+#pragma unroll
+                            for (int u = 0; u < TT; ++u) {
+                                const int t = min(t0 + 16 * u + m, T - 1);
+                                A.xv[h][u] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * D + off);
+                            }
+                        }
+                    }
+                }
+                compute(A, kk);
             }
         }
     }
@@ -664,13 +702,13 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
         const int et = 16 * p.expert_tiles, tt = 16 * p.token_tiles;
         const dim3 g((p.E + et - 1) / et, (p.T + tt - 1) / tt, p.splits);
         if (p.token_tiles == 1)
-            hipLaunchKernelGGL((router_logits_kernel<1, 1, 4>), g, dim3(kRouterWaves * 64), 0,
+            hipLaunchKernelGGL((router_logits_kernel<1, 1, 4, false>), g, dim3(kRouterWaves * 64), 0,
                                stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
         else if (p.expert_tiles == 2)
-            hipLaunchKernelGGL((router_logits_kernel<4, 2, 4>), g, dim3(kRouterWaves * 64), 0,
+            hipLaunchKernelGGL((router_logits_kernel<4, 2, 4, false>), g, dim3(kRouterWaves * 64), 0,
                                stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
         else
-            hipLaunchKernelGGL((router_logits_kernel<4, 4, 2>), g, dim3(kRouterWaves * 64), 0,
+            hipLaunchKernelGGL((router_logits_kernel<4, 4, 1, true>), g, dim3(kRouterWaves * 64), 0,
                                stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
     }
     if (p.T <= kSmallTokens && p.T * p.E <= kSmallLogits) {
