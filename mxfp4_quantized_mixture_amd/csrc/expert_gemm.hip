@@ -317,7 +317,7 @@ __global__ __launch_bounds__(64 * WR * WP, 8 / (WR * WP)) void expert_gemm_kerne
     uint8_t* dummy = lds + kBufs * kBufBytes + (size_t)WR * NA * K + (wave & 7) * 1024;
     __syncthreads();
 
-    // Staging: piece p = tid + 256 c (p < 128 kRowPieces) is 16-byte piece
+    // Staging: piece p = tid + kGemmThreads c (p < 128 kRowPieces) is 16-byte piece
     // p % kRowPieces of row p / kRowPieces's step chunk, loaded straight into
     // byte 16 p of the LDS slot (direct global -> LDS loads: a wave's 64
     // pieces land contiguously at a wave-uniform destination).
