@@ -185,9 +185,12 @@ __global__ __launch_bounds__(256) void mxfp4_dequantize_kernel(
 
 // Packed code layout for the expert kernels: for each 32-row fragment f and
 // each 64-element contraction step t, the fragment's 32 rows x 32 bytes of
-// that step are one contiguous 1 KiB chunk, chunks in (f, t) order:
-//   packed[(f * K/64 + t) * 1024 + r * 32 + j] = q[(32 f + r) * K/2 + 32 t + j].
-// One thread per 16 bytes of output (coalesced writes, 32-byte gathers).
+// that step are one contiguous 1 KiB chunk, chunks in (f, t) order, the
+// first 16 bytes (elements 0..31 of the step) of all 32 rows before the
+// second 16 bytes:
+//   packed[(f * K/64 + t) * 1024 + 512 h + 16 r + b] = q[(32 f + r) * K/2 + 32 t + 16 h + b]
+// (h = 0, 1; b < 16), so lane l = 32 h + r of a wavefront finds its 16 bytes
+// at 16 l.  One thread per 16 bytes of output (coalesced writes).
 __global__ __launch_bounds__(256) void mxfp4_pack_kernel(const uint8_t* __restrict__ q,
                                                          uint8_t* __restrict__ out,
                                                          int64_t n16, int64_t K) {
