@@ -276,13 +276,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*fp8->f32",
+        "dtype": "mxfp4*fp8->f32" if decode else "mxfp4*fp8->f32 (gate/up), f16*f16->f32 (down)",
         "data": "synthetic",
         "config": {"workload": cfg.description, "name": cfg.name, "tokens": cfg.T,
                    "d_model": cfg.D, "d_ff": cfg.F, "experts": cfg.E, "top_k": cfg.k,
                    "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)",
-                   "matrix_cores": "block-scaled mfma: mxfp4 weights x fp8 residual terms "
-                                   "of the activations, fp32 accumulate",
+                   "matrix_cores": ("block-scaled mfma: mxfp4 weights x fp8 residual terms "
+                                    "of the activations, fp32 accumulate") if decode else
+                                   ("gate/up: block-scaled mfma, mxfp4 weights x 2 fp8 terms "
+                                    "of x; down: f16 mfma, fp16 h x W2 codes converted to "
+                                    "fp16 per tile; fp32 accumulate"),
                    "expert_algorithm": "weight streaming" if decode else "grouped gemm",
                    "weight_layout": "packed 32x64 fragments" if packed else "row-major",
                    "touched_experts": work["touched"], "weight_copies_rotated": NCOPIES,
