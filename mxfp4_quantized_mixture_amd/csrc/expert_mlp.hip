@@ -626,6 +626,9 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
 }
 
 // out[t, d] = bf16( sum_j w[t, j] * y[pos[t*k + j], d] ), slots in order.
+// All k slots' positions and weights are loaded first, then all k rows, so
+// a thread waits for two memory round trips, not 2 k.
+constexpr int kCombineMaxK = 8;
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, const float* __restrict__ topk_w,
     const int32_t* __restrict__ pos, int T, int D, int k, uint16_t* __restrict__ out) {
@@ -634,13 +637,26 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const int t = (int)(i / q), d4 = (int)(i % q);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            const int p = t * k + j;
-            const float wv = topk_w[p];
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(y + (size_t)pos[p] * D + d4 * 4);
+        int pr[kCombineMaxK];
+        float wv[kCombineMaxK];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(wv, v[c], acc[c]);
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+                pr[j] = pos[t * k + j];
+                wv[j] = topk_w[t * k + j];
+            }
+        }
+        f32x4_t v[kCombineMaxK];
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j)
+            if (j < k) v[j] = *reinterpret_cast<const f32x4_t*>(y + (size_t)pr[j] * D + d4 * 4);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(wv[j], v[j][c], acc[c]);
+            }
         }
         uint2 o;
         o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
