@@ -78,13 +78,17 @@ typedef enum {
 
 /* How moe_expert_mlp_ex runs the experts (moe_expert_mlp: automatic). */
 typedef enum {
-    MOE_MLP_AUTO = 0,          /* grouped GEMM when D % 64 == 0, F % 64 == 0 and
-                                  T*k >= 32*E (32 pairs per expert on average),
-                                  weight streaming otherwise */
+    MOE_MLP_AUTO = 0,          /* grouped GEMM when it takes the shape (see
+                                  MOE_MLP_GROUPED_GEMM) and T*k >= 32*E (32 pairs
+                                  per expert on average), weight streaming
+                                  otherwise */
     MOE_MLP_STREAM = 1,        /* weight streaming: each touched expert's weights
                                   are read once per group of 16 of its pairs */
     MOE_MLP_GROUPED_GEMM = 2,  /* tiled grouped GEMM over 128-pair tiles; needs
-                                  D % 64 == 0 and F % 64 == 0 (else MOE_ERR_SHAPE) */
+                                  D % 64 == 0, F % 64 == 0, D <= 8192, F <= 7232
+                                  (LDS budget), and T*(D/64)*144, T*k*F*2 and
+                                  E*F*D under 4 GiB (32-bit offsets), else
+                                  MOE_ERR_SHAPE */
     MOE_MLP_WEIGHTS_PACKED = 0x100  /* flag, OR-ed into the algorithm: w13_q and w2_q
                                   are in the layout mxfp4_pack writes (the scales
                                   are unchanged); needs D % 64 == 0, F % 64 == 0

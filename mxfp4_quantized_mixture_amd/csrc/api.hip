@@ -128,6 +128,7 @@ moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const ui
         !pair_pos || !out)
         return MOE_ERR_NULL;
     const moe::MlpPlan plan = moe::plan_mlp(T, D, F, E, k);
+    if (base == MOE_MLP_GROUPED_GEMM && !plan.gemm_ok) return MOE_ERR_SHAPE;
     if (packed && !plan.packed_ok) return MOE_ERR_SHAPE;
     if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||

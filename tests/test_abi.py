@@ -146,6 +146,9 @@ def test_mlp_algorithm_validation(L):
     assert _mlp_ex(L, -1) == ENUM
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, D=96) == SHAPE      # grouped GEMM needs D % 64
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=160) == SHAPE     # ... and F % 64
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=7296) == SHAPE    # down GEMM's LDS budget
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, D=8256) == SHAPE    # contraction limit
+    assert _mlp_ex(L, moe.MLP_STREAM, F=7296, out=None) == NULL # streaming takes any F
     assert _mlp_ex(L, moe.MLP_STREAM, out=None) == NULL
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, out=None) == NULL
     P = moe.MLP_WEIGHTS_PACKED
