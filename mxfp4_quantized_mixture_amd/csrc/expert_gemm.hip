@@ -114,12 +114,20 @@ __global__ __launch_bounds__(256) void split_terms_kernel(const uint16_t* __rest
     const uint16_t* p = src + (size_t)row * K + (size_t)s * 64;
     uint8_t* o = tq + ((size_t)row * S + s) * term_chunk(NT);
     uint32_t sc_bytes[2] = {0u, 0u};
+    // the whole 128-byte step is loaded before any of it is converted
+    u32x4_t raws[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            raws[hb][c] = *reinterpret_cast<const u32x4_t*>(p + hb * 32 + c * 8);
+    __builtin_amdgcn_sched_barrier(0);                   // (keep the loads together)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         float v[32];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(p + hb * 32 + c * 8);
+            const u32x4_t raw = raws[hb][c];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 v[c * 8 + 2 * h] = bf16_to_f32(raw[h] & 0xFFFFu);
