@@ -332,6 +332,7 @@ __device__ __forceinline__ void wave_topk(float v0, float v1, float v2, float v3
 // Top-k, softmax over the selected logits and the chunk histogram: one
 // wavefront per token of the block's 16-token chunk (logit = the S router
 // slices summed in order).
+template <int kMaxS>
 __global__ __launch_bounds__(kChunkTokens * 64) void route_topk_kernel(
     const float* __restrict__ P, int S, int T, int E, int k, float* __restrict__ logits_out,
     int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ chunk_counts) {
@@ -339,17 +340,18 @@ __global__ __launch_bounds__(kChunkTokens * 64) void route_topk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < kMaxE; i += blockDim.x) cnt[i] = 0;
     const int t = blockIdx.x * kChunkTokens + wave;
-    constexpr int kMaxS = 16;
     float v[4];
     {
+        // unconditional loads (clamped slice, token and expert; the extra
+        // values are discarded), so the compiler issues them all at once
         float part[4][kMaxS];
+        const int tc = min(t, T - 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int e = lane + 64 * q;
-            const bool ok = t < T && e < E;
+            const int ec = min(lane + 64 * q, E - 1);
 #pragma unroll
             for (int sp = 0; sp < kMaxS; ++sp)
-                part[q][sp] = (ok && sp < S) ? P[((int64_t)sp * T + t) * E + e] : 0.f;
+                part[q][sp] = P[((int64_t)min(sp, S - 1) * T + tc) * E + ec];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -725,8 +727,14 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
         }
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(route_topk_kernel, dim3(p.chunks), dim3(kChunkTokens * 64), 0, stream, P,
-                       p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts);
+    // (slice loads are unconditional up to the template's bound: 4 when the
+    // router used at most 4 slices)
+    if (p.splits <= 4)
+        hipLaunchKernelGGL(route_topk_kernel<4>, dim3(p.chunks), dim3(kChunkTokens * 64), 0,
+                           stream, P, p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts);
+    else
+        hipLaunchKernelGGL(route_topk_kernel<16>, dim3(p.chunks), dim3(kChunkTokens * 64), 0,
+                           stream, P, p.splits, p.T, p.E, p.k, logits_out, ids, w, chunk_counts);
     const int pairs = p.T * p.k;
     if (pairs <= kFinishMaxPairs) {
         hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, p.E,
