@@ -1,5 +1,5 @@
 """Thin Python binding of libmoe_mxfp4 (MXFP4 mixture-of-experts MLP layer
-for AMD MI355X / gfx950).
+for AMD MI355X / gfx950), ABI version 2.
 
 Every step of the layer runs in the HIP kernels of libmoe_mxfp4.so; this
 module only marshals torch tensors (device memory and the current stream)
@@ -32,6 +32,7 @@ __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "mxfp4_pack", "moe_route", "moe
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
+ABI_VERSION = 2
 SCALE_FLOOR_DIV6 = 0
 SCALE_OCP = 1
 SCALE_CEIL_DIV6 = 2
@@ -59,15 +60,18 @@ def lib() -> ctypes.CDLL:
                 f"{LIB_PATH} is not built; run `python -m mxfp4_quantized_mixture_amd.build` "
                 "(there is no CPU fallback)")
         L = ctypes.CDLL(LIB_PATH)
+        if L.moe_abi_version() != ABI_VERSION:
+            raise ImportError("%s has ABI version %d, this binding needs %d: rebuild it"
+                              % (LIB_PATH, L.moe_abi_version(), ABI_VERSION))
         P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_abi_version.argtypes = []
         L.moe_abi_version.restype = ctypes.c_int
-        L.mxfp4_quantize.argtypes = [P, i64, i64, ctypes.c_int, P, P, P]
+        L.mxfp4_quantize.argtypes = [P, i64, i64, P, P, ctypes.c_int, P]
         L.mxfp4_quantize.restype = ctypes.c_int
-        L.mxfp4_quantize_ex.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_uint64, P, P, P]
+        L.mxfp4_quantize_ex.argtypes = [P, i64, i64, P, P, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_uint64, P]
         L.mxfp4_quantize_ex.restype = ctypes.c_int
         L.mxfp4_dequantize.argtypes = [P, P, i64, i64, P, P]
         L.mxfp4_dequantize.restype = ctypes.c_int
@@ -80,7 +84,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_mlp_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         L.moe_expert_mlp_workspace_size.restype = sz
         L.moe_expert_mlp.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
-                                     P, P, sz, P, P]
+                                     P, P, sz, P]
         L.moe_expert_mlp.restype = ctypes.c_int
         L.moe_expert_mlp_ex.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                         P, P, sz, ctypes.c_int, P, P]
@@ -119,8 +123,8 @@ def mxfp4_quantize(w: torch.Tensor, rule: int = SCALE_FLOOR_DIV6, stochastic: bo
     q = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
     s = torch.empty(*w.shape[:-1], K // 32, dtype=torch.uint8, device=w.device)
     _check("mxfp4_quantize", lib().mxfp4_quantize_ex(
-        _dev(w, "w", torch.bfloat16), rows, K, rule, ROUND_STOCHASTIC if stochastic else
-        ROUND_NEAREST_EVEN, int(seed) & (2**64 - 1), _dev(q, "q"), _dev(s, "s"),
+        _dev(w, "w", torch.bfloat16), rows, K, _dev(q, "q"), _dev(s, "s"), rule,
+        ROUND_STOCHASTIC if stochastic else ROUND_NEAREST_EVEN, int(seed) & (2**64 - 1),
         _stream(w.device)))
     return q, s
 

@@ -1,12 +1,42 @@
 // api.hip -- the exported C ABI of libmoe_mxfp4 (declared in
-// include/moe_mxfp4.h): argument validation, workspace carving, launches.
-// Every check happens before anything is enqueued.
+// include/moe_mxfp4.h): argument validation, the device check, workspace
+// carving, launches.  Every check happens before anything is enqueued.
+#include <atomic>
+#include <cstring>
+
 #include "moe_mxfp4.h"
 #include "launch.h"
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The device a call's work would run on (the stream's, or the current one
+// for the null stream) must be a gfx950.  The answer is cached per device
+// id: 0 = not asked yet, 1 = gfx950, 2 = something else.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_kind[kMaxDevices];
+
+moe_status_t check_device(hipStream_t stream) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_ERR_DEVICE;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return MOE_ERR_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+    int kind = g_device_kind[dev].load(std::memory_order_acquire);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
+        // gcnArchName is e.g. "gfx950:sramecc+:xnack-"
+        kind = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                       (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':')
+                   ? 1 : 2;
+        g_device_kind[dev].store(kind, std::memory_order_release);
+    }
+    return kind == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -28,15 +58,16 @@ const char* moe_status_string(int status) {
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_ENUM: return "unknown scale rule or algorithm";
         case MOE_ERR_HIP: return "kernel launch failed";
+        case MOE_ERR_DEVICE: return "no gfx950 (MI355X) device for the stream";
         case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         default: return "unknown status";
     }
 }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-moe_status_t mxfp4_quantize_ex(const uint16_t* w, int64_t rows, int64_t K, int scale_rule,
-                               int rounding, uint64_t seed, uint8_t* q, uint8_t* s,
+moe_status_t mxfp4_quantize_ex(const uint16_t* w, int64_t rows, int64_t K, uint8_t* q,
+                               uint8_t* s, int scale_rule, int rounding, uint64_t seed,
                                hipStream_t stream) {
     if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
     if (scale_rule != MXFP4_SCALE_FLOOR_DIV6 && scale_rule != MXFP4_SCALE_OCP &&
@@ -47,12 +78,13 @@ moe_status_t mxfp4_quantize_ex(const uint16_t* w, int64_t rows, int64_t K, int s
     if (rows == 0) return MOE_OK;
     if (!w || !q || !s) return MOE_ERR_NULL;
     if (!aligned16(w) || !aligned16(q)) return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
     return hip_status(moe::launch_quantize(w, rows, K, scale_rule, rounding, seed, q, s, stream));
 }
 
-moe_status_t mxfp4_quantize(const uint16_t* w, int64_t rows, int64_t K, int scale_rule,
-                            uint8_t* q, uint8_t* s, hipStream_t stream) {
-    return mxfp4_quantize_ex(w, rows, K, scale_rule, MXFP4_ROUND_NEAREST_EVEN, 0, q, s, stream);
+moe_status_t mxfp4_quantize(const uint16_t* w, int64_t rows, int64_t K, uint8_t* q, uint8_t* s,
+                            int scale_rule, hipStream_t stream) {
+    return mxfp4_quantize_ex(w, rows, K, q, s, scale_rule, MXFP4_ROUND_NEAREST_EVEN, 0, stream);
 }
 
 moe_status_t mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K,
@@ -61,6 +93,7 @@ moe_status_t mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, 
     if (rows == 0) return MOE_OK;
     if (!q || !s || !out) return MOE_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
     return hip_status(moe::launch_dequantize(q, s, rows, K, out, stream));
 }
 
@@ -73,6 +106,7 @@ moe_status_t mxfp4_pack(const uint8_t* q, int64_t rows, int64_t K, uint8_t* out,
     const uintptr_t a0 = (uintptr_t)q, a1 = a0 + (uintptr_t)(rows * (K / 2));
     const uintptr_t b0 = (uintptr_t)out, b1 = b0 + (uintptr_t)(rows * (K / 2));
     if (a0 < b1 && b0 < a1) return MOE_ERR_SHAPE;       // in place or overlapping
+    if (const moe_status_t d = check_device(stream)) return d;
     return hip_status(moe::launch_pack(q, rows, K, out, stream));
 }
 
@@ -92,6 +126,7 @@ moe_status_t moe_route(const uint16_t* x, const float* wr, const float* br, int3
     const moe::RoutePlan plan = moe::plan_route(T, D, E, k);
     if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(wr) || !aligned16(ws)) return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
     return hip_status(moe::launch_route(plan, x, wr, br, topk_ids, topk_w, counts, offsets,
                                         sorted_pairs, pair_pos, logits_out, ws, stream));
 }
@@ -106,10 +141,10 @@ moe_status_t moe_expert_mlp(const uint16_t* x, const uint8_t* w13_q, const uint8
                             const int32_t* offsets, const int32_t* sorted_pairs,
                             const int32_t* pair_pos, int32_t T, int32_t D, int32_t F,
                             int32_t E, int32_t k, uint16_t* out, void* ws, size_t ws_bytes,
-                            hipEvent_t* stage_events, hipStream_t stream) {
+                            hipStream_t stream) {
     return moe_expert_mlp_ex(x, w13_q, w13_s, w2_q, w2_s, topk_w, offsets, sorted_pairs,
-                             pair_pos, T, D, F, E, k, out, ws, ws_bytes, MOE_MLP_AUTO,
-                             stage_events, stream);
+                             pair_pos, T, D, F, E, k, out, ws, ws_bytes, MOE_MLP_AUTO, nullptr,
+                             stream);
 }
 
 moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
@@ -123,17 +158,19 @@ moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const ui
     if (base != MOE_MLP_AUTO && base != MOE_MLP_STREAM && base != MOE_MLP_GROUPED_GEMM)
         return MOE_ERR_ENUM;
     if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return MOE_ERR_SHAPE;
-    if (base == MOE_MLP_GROUPED_GEMM && (D % 64 != 0 || F % 64 != 0)) return MOE_ERR_SHAPE;
     if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !offsets || !sorted_pairs ||
         !pair_pos || !out)
         return MOE_ERR_NULL;
     const moe::MlpPlan plan = moe::plan_mlp(T, D, F, E, k);
     if (base == MOE_MLP_GROUPED_GEMM && !plan.gemm_ok) return MOE_ERR_SHAPE;
+    if (base == MOE_MLP_STREAM && !plan.stream_ok) return MOE_ERR_SHAPE;
+    if (base == MOE_MLP_AUTO && !plan.stream_ok && !plan.gemm_ok) return MOE_ERR_SHAPE;
     if (packed && !plan.packed_ok) return MOE_ERR_SHAPE;
     if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
         !aligned16(w2_s) || !aligned16(out) || !aligned16(ws))
         return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
     return hip_status(moe::launch_mlp(plan, base, packed, x, w13_q, w13_s, w2_q, w2_s, topk_w,
                                       offsets, sorted_pairs, pair_pos, out, ws, stage_events,
                                       stream));

@@ -18,8 +18,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(32 * sizeof(float)))) float f32x32_t;
+typedef __attribute__((__vector_size__(6 * sizeof(uint32_t)))) uint32_t u32x6_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
-// fp32 -> bf16 bits, round half to even (finite inputs).
 // Workgroup barrier ordering LDS accesses only.  __syncthreads() also
 // orders global memory, which makes every wavefront wait for all of its
 // outstanding loads (the load counter does not tell loads from stores).
@@ -29,6 +31,7 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// fp32 -> bf16 bits, round half to even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -115,6 +118,102 @@ __device__ __forceinline__ void sub4_fp8(float* v, uint32_t q, float sc) {
     v[1] -= __builtin_amdgcn_cvt_f32_fp8((int)q, 1) * sc;
     v[2] -= __builtin_amdgcn_cvt_f32_fp8((int)q, 2) * sc;
     v[3] -= __builtin_amdgcn_cvt_f32_fp8((int)q, 3) * sc;
+}
+
+// ---------------------------------------------------------------------------
+// fp6 (E2M3) residual terms.  E2M3: 1 sign, 2 exponent (bias 1) and 3
+// mantissa bits; magnitudes k/8 (k = 0..7, exponent field 0) and
+// 2^(e-1) (1 + m/8) (e = 1..3), largest 7.5.  A block of 32 values is carried
+// as kFp6Terms terms, term t + 1 holding the exact fp32 residual of term t,
+// each with its own E8M0 scale 2^s.  s is chosen so the term's largest
+// magnitude rounds into [4, 7.5]; every element's rounding error is then at
+// most 1/16 of that magnitude, so each term removes all but 2^-4 of what is
+// left and three terms leave at most 2^-12 of the block's largest magnitude,
+// at any magnitude the scales reach (2^-126 .. 2^126).
+//
+// Codes of a block: element i at bits 6i .. 6i + 5 of 6 dwords, the order in
+// which the gfx950 block-scaled products read an fp6 operand (lane (n, g)
+// of the 32x32x64 product: column n, K = 32 g .. 32 g + 31).  The hardware
+// conversion v_cvt_scalef32_2xpk16_fp6_f32 rounds v / scale to nearest even
+// and writes its first source's 16 values to the even elements and its
+// second source's to the odd ones (both checked bit for bit with in-bounds
+// probes, ties included); its inverse v_cvt_scalef32_pk32_f32_fp6 returns
+// code value * scale exactly.
+// ---------------------------------------------------------------------------
+constexpr int kFp6Terms = 3;
+
+// s in [-126, 126] such that amax * 2^-s, rounded to 4 significant bits, lies
+// in [4, 7.5]: floor(log2 amax) - 2, plus 1 when the mantissa is at least
+// 1.9375 (which would round to 8, past the largest E2M3 value).  amax = 0
+// gives -126 (all codes of the block are then zero).
+__device__ __forceinline__ int e2m3_term_exponent(float amax) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, amax);
+    const int s = (int)(b >> 23) - 129 + ((b & 0x7FFFFFu) >= 0x780000u ? 1 : 0);
+    return s < -126 ? -126 : (s > 126 ? 126 : s);
+}
+
+// 2^s for s in [-126, 127] (normal fp32)
+__device__ __forceinline__ float exp2i_normal(int s) {
+    return __builtin_bit_cast(float, (uint32_t)(127 + s) << 23);
+}
+
+// The kFp6Terms terms of one 32-element block v (v is left holding the
+// final residual): codes[t] (6 dwords) and E8M0 scale bytes sb[t].
+__device__ __forceinline__ void fp6_block_terms(float (&v)[32], u32x6_t (&codes)[kFp6Terms],
+                                                uint32_t (&sb)[kFp6Terms]) {
+#pragma unroll
+    for (int t = 0; t < kFp6Terms; ++t) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const int s = e2m3_term_exponent(amax);
+        const float sc = exp2i_normal(s);
+        f32x16_t ev, od;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            ev[i] = v[2 * i];
+            od[i] = v[2 * i + 1];
+        }
+        codes[t] = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, sc);
+        sb[t] = (uint32_t)(s + 127);
+        if (t + 1 < kFp6Terms) {
+            const f32x32_t back = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(codes[t], sc);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] -= back[i];
+        }
+    }
+}
+
+// One 64-element step of an fp6 term row (kTermStep bytes, as 40 dwords):
+// bytes 48 t + 16 h .. + 15 hold the first 16 code bytes of term t of the
+// step's block h (h = 0, 1), bytes 48 t + 32 + 8 h .. + 7 its last 8, byte
+// 144 + 2 t + h its E8M0 scale; bytes 150 .. 159 are zero.  A lane (n, g) of
+// the 32x32x64 product thus reads its term-t operand of row n as one 16-byte
+// and one 8-byte piece, and its scale from the dword at 144 + 4 (t / 2).
+constexpr int kTermStep = 160;
+static_assert(kFp6Terms == 3 && 48 * kFp6Terms + 2 * kFp6Terms <= kTermStep, "term step layout");
+
+__device__ __forceinline__ void fp6_encode_step(float (&v)[64], uint32_t (&out)[kTermStep / 4]) {
+    uint32_t sb[2][kFp6Terms];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float blk[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) blk[i] = v[32 * h + i];
+        u32x6_t codes[kFp6Terms];
+        fp6_block_terms(blk, codes, sb[h]);
+#pragma unroll
+        for (int t = 0; t < kFp6Terms; ++t) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[12 * t + 4 * h + w] = codes[t][w];
+            out[12 * t + 8 + 2 * h] = codes[t][4];
+            out[12 * t + 9 + 2 * h] = codes[t][5];
+        }
+    }
+    out[36] = sb[0][0] | (sb[1][0] << 8) | (sb[0][1] << 16) | (sb[1][1] << 24);
+    out[37] = sb[0][2] | (sb[1][2] << 8);
+    out[38] = 0u;
+    out[39] = 0u;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }

@@ -1,25 +1,20 @@
-// expert_mlp.hip -- SwiGLU experts on MXFP4 weights and the weighted combine,
-// for gfx950.
+// expert_mlp.hip -- SwiGLU experts on MXFP4 weights by weight streaming, and
+// the weighted combine, for gfx950.
 //
 // Per routed pair p = t*k + j of expert e ("Welcome GPT OSS", section 4:
 // SwiGLU experts, softmax-after-topk weights; no shared expert per the talk
 // summary's Q&A):  g = Wg_e x_t,  u = Wu_e x_t,  h = silu(g) * u,
 // y_p = W2_e h,  out[t] = sum_j w[t, j] * y_p.
-// The weights stay MXFP4 in HBM and are widened to bf16 / fp16 in registers
-// right before the matrix-core product ("Tricks", section 8: GEMMs that
-// understand 32-element blocks and their scales; talk summary, "Hardware
-// optimisation": store low precision, upcast at compute).
+// The weights stay MXFP4 in HBM and enter the matrix cores as stored ("Tricks",
+// section 8: GEMMs that understand 32-element blocks and their scales; talk
+// summary, "Hardware optimisation": store low precision, widen only inside
+// the arithmetic).
 //
-// Weight-streaming kernels (every expert's rows are read once per 16-token
-// group): a block owns a range of 16-row weight tiles of one expert; its four
-// wavefronts split the contraction dimension, hold their slice of the token
-// activations in registers, and reduce through LDS in a fixed order.
-//
-// K permutation: a "super-step" covers 4 MXFP4 blocks (128 K).  Lane group
-// g = lane / 16 owns block 4*ss + g and feeds its 32 elements to four 16x16x32
-// products, 8 per product.  The A (weights) and B (activations) operands use
-// the same permutation, so the contraction is unchanged, and every lane loads
-// one whole 16-byte block of codes plus its one scale byte.
+// These kernels serve batches in which experts receive few tokens (decode):
+// every touched expert's weights are read once per group of 16 of its pairs,
+// and the kernels are bound by that weight stream.  The grouped GEMMs of
+// expert_gemm.hip serve the rest (and the shapes these kernels' LDS budget
+// does not take).  h travels between the two streaming kernels in fp32.
 #include <algorithm>
 #include <type_traits>
 
@@ -27,178 +22,6 @@
 #include "launch.h"
 
 namespace moe {
-
-constexpr int kMaxSS = 6;    // super-steps of activations a wave keeps in registers
-
-// h[row, f] for the rows of expert e (sorted order), fp16.
-__global__ __launch_bounds__(256) void gateup_stream_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13q,
-    const uint8_t* __restrict__ w13s, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted, int D, int F, int k, int bpe,
-    _Float16* __restrict__ h) {
-    __shared__ f32x4_t red[2][4][2][64];
-    const int e = blockIdx.x / bpe, part = blockIdx.x % bpe;
-    const int row0 = offsets[e];
-    const int ne = offsets[e + 1] - row0;
-    if (ne <= 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int nblk = D / 32;
-    const int nss = (nblk + 3) / 4;
-    const int ss_beg = nss * wave / 4, ss_end = nss * (wave + 1) / 4;
-    const int ntiles = F / 16;
-    const int tile_beg = ntiles * part / bpe, tile_end = ntiles * (part + 1) / bpe;
-    const size_t rowbytes = (size_t)D / 2;
-    const uint8_t* qe = w13q + (size_t)e * 2 * F * rowbytes;
-    const uint8_t* se = w13s + (size_t)e * 2 * F * nblk;
-    int par = 0;
-
-    for (int tg = 0; tg < ne; tg += 16) {
-        const int r = tg + m;
-        const bool tok_ok = r < ne;
-        const int tok = tok_ok ? sorted[row0 + r] / k : 0;
-        const uint16_t* xrow = x + (size_t)tok * D;
-        int loaded = -1;
-        bf16x8_t xf[kMaxSS][4];
-        for (int tile = tile_beg; tile < tile_end; ++tile) {
-            f32x4_t acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* qg = qe + (size_t)(tile * 16 + m) * rowbytes;
-            const uint8_t* qu = qe + (size_t)(F + tile * 16 + m) * rowbytes;
-            const uint8_t* sg = se + (size_t)(tile * 16 + m) * nblk;
-            const uint8_t* su = se + (size_t)(F + tile * 16 + m) * nblk;
-            for (int kc = ss_beg; kc < ss_end; kc += kMaxSS) {
-                if (kc != loaded) {
-#pragma unroll
-                    for (int i = 0; i < kMaxSS; ++i) {
-                        const int blk = (kc + i) * 4 + g;
-                        const bool ok = tok_ok && kc + i < ss_end && blk < nblk;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x4_t v = {0u, 0u, 0u, 0u};
-                            if (ok) v = *reinterpret_cast<const u32x4_t*>(xrow + blk * 32 + j * 8);
-                            xf[i][j] = as_bf16x8(v);
-                        }
-                    }
-                    loaded = kc;
-                }
-#pragma unroll
-                for (int i = 0; i < kMaxSS; ++i) {
-                    if (kc + i < ss_end) {
-                        const int blk = (kc + i) * 4 + g;
-                        u32x4_t wg = {0u, 0u, 0u, 0u}, wu = {0u, 0u, 0u, 0u};
-                        uint32_t bg = 127u, bu = 127u;
-                        if (blk < nblk) {
-                            wg = *reinterpret_cast<const u32x4_t*>(qg + blk * 16);
-                            wu = *reinterpret_cast<const u32x4_t*>(qu + blk * 16);
-                            bg = sg[blk];
-                            bu = su[blk];
-                        }
-                        const float scg = e8m0_to_f32(bg), scu = e8m0_to_f32(bu);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            acc_g = mfma_bf16(fp4x8_to_bf16x8(wg[j], scg), xf[i][j], acc_g);
-                            acc_u = mfma_bf16(fp4x8_to_bf16x8(wu[j], scu), xf[i][j], acc_u);
-                        }
-                    }
-                }
-            }
-            red[par][wave][0][lane] = acc_g;
-            red[par][wave][1][lane] = acc_u;
-            __syncthreads();
-            if (wave == 0 && tok_ok) {
-                f32x4_t sg4 = red[par][0][0][lane], su4 = red[par][0][1][lane];
-#pragma unroll
-                for (int w = 1; w < 4; ++w) {
-                    sg4 += red[par][w][0][lane];
-                    su4 += red[par][w][1][lane];
-                }
-                typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
-                f16x4_t hv;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) hv[q] = (_Float16)(silu_f32(sg4[q]) * su4[q]);
-                *reinterpret_cast<f16x4_t*>(h + (size_t)(row0 + r) * F + tile * 16 + 4 * g) = hv;
-            }
-            par ^= 1;
-        }
-    }
-}
-
-// y[row, d] = W2_e h[row] (fp32), rows of expert e in sorted order.
-__global__ __launch_bounds__(256) void down_stream_kernel(
-    const _Float16* __restrict__ h, const uint8_t* __restrict__ w2q,
-    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ offsets, int D, int F,
-    int bpe, float* __restrict__ y) {
-    __shared__ f32x4_t red[2][4][64];
-    const int e = blockIdx.x / bpe, part = blockIdx.x % bpe;
-    const int row0 = offsets[e];
-    const int ne = offsets[e + 1] - row0;
-    if (ne <= 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int nblk = F / 32;
-    const int nss = (nblk + 3) / 4;
-    const int ss_beg = nss * wave / 4, ss_end = nss * (wave + 1) / 4;
-    const int ntiles = D / 16;
-    const int tile_beg = ntiles * part / bpe, tile_end = ntiles * (part + 1) / bpe;
-    const size_t rowbytes = (size_t)F / 2;
-    const uint8_t* qe = w2q + (size_t)e * D * rowbytes;
-    const uint8_t* se = w2s + (size_t)e * D * nblk;
-    int par = 0;
-
-    for (int tg = 0; tg < ne; tg += 16) {
-        const int r = tg + m;
-        const bool tok_ok = r < ne;
-        const _Float16* hrow = h + (size_t)(row0 + (tok_ok ? r : 0)) * F;
-        int loaded = -1;
-        f16x8_t hf[kMaxSS][4];
-        for (int tile = tile_beg; tile < tile_end; ++tile) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* qd = qe + (size_t)(tile * 16 + m) * rowbytes;
-            const uint8_t* sd = se + (size_t)(tile * 16 + m) * nblk;
-            for (int kc = ss_beg; kc < ss_end; kc += kMaxSS) {
-                if (kc != loaded) {
-#pragma unroll
-                    for (int i = 0; i < kMaxSS; ++i) {
-                        const int blk = (kc + i) * 4 + g;
-                        const bool ok = tok_ok && kc + i < ss_end && blk < nblk;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x4_t v = {0u, 0u, 0u, 0u};
-                            if (ok) v = *reinterpret_cast<const u32x4_t*>(hrow + blk * 32 + j * 8);
-                            hf[i][j] = as_f16x8(v);
-                        }
-                    }
-                    loaded = kc;
-                }
-#pragma unroll
-                for (int i = 0; i < kMaxSS; ++i) {
-                    if (kc + i < ss_end) {
-                        const int blk = (kc + i) * 4 + g;
-                        u32x4_t wd = {0u, 0u, 0u, 0u};
-                        uint32_t bd = 127u;
-                        if (blk < nblk) {
-                            wd = *reinterpret_cast<const u32x4_t*>(qd + blk * 16);
-                            bd = sd[blk];
-                        }
-                        const float sc = e8m0_to_f32(bd);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc = mfma_f16(fp4x8_to_f16x8(wd[j], sc), hf[i][j], acc);
-                    }
-                }
-            }
-            red[par][wave][lane] = acc;
-            __syncthreads();
-            if (wave == 0 && tok_ok) {
-                f32x4_t s4 = red[par][0][lane];
-#pragma unroll
-                for (int w = 1; w < 4; ++w) s4 += red[par][w][lane];
-                *reinterpret_cast<f32x4_t*>(y + (size_t)(row0 + r) * D + tile * 16 + 4 * g) = s4;
-            }
-            par ^= 1;
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Balanced weight-streaming kernels.
@@ -218,12 +41,14 @@ constexpr int kMaxWaveTiles = 4;       // tile outputs a wavefront holds in regi
 // Staged activations.  The weights enter the matrix cores exactly as stored
 // (E2M1 codes + E8M0 block scales, v_mfma_scale_f32_16x16x128_f8f6f4 with an
 // fp4 A operand), so the activations must be fp8: each activation row is
-// split into NT E4M3 terms, term t+1 carrying the rounding residual of term
-// t, each with its own E8M0 scale per 32-element block.  A value with b
-// significant bits is represented exactly by ceil(b / 4) terms when it lies
-// within 13 binades of its block's largest magnitude (bf16 x: 2 terms;
-// fp16 h: 3 terms); smaller elements keep an error below 2^-21 of that
-// magnitude.
+// split into NT E4M3 terms, term t+1 carrying the exact fp32 rounding
+// residual of term t, each with its own E8M0 scale per 32-element block
+// (the block's largest magnitude scaled into [128, 256)).  Each term leaves
+// at most 2^-4 of an element's remaining magnitude while that lies within 13
+// binades of the block's largest, so bf16 x (8 significant bits) is exact
+// in 2 terms there and fp32 h keeps a relative error below 2^-12 after 3;
+// elements further down keep an absolute error below 2^-21 of the block's
+// largest magnitude.  The E8M0 scales reach any fp32 magnitude.
 //
 // Operand layouts of the 16x16x128 scaled product (lane l, m = l % 16,
 // g = l / 16): A lane holds row m, K = 32 g .. 32 g + 31 (one MXFP4 block,
@@ -242,13 +67,8 @@ __device__ __forceinline__ f32x4_t mfma_fp4w_fp8x(u32x4_t w, int wscale, const u
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 0, 0, wscale, 0, bscale);
 }
 
-__device__ __forceinline__ float act_to_f32(uint16_t v, bool is_bf16) {
-    return is_bf16 ? __builtin_bit_cast(float, (uint32_t)v << 16)
-                   : (float)__builtin_bit_cast(_Float16, v);
-}
-
 // Stage the unit's rows (pairs row0 .. row0 + nvalid - 1 in sorted order;
-// gathered bf16 x rows for gate/up, contiguous fp16 h rows for down) as NT
+// gathered bf16 x rows for gate/up, contiguous fp32 h rows for down) as NT
 // fp8 terms.  One thread per (row, 32-element block); rows past nvalid and
 // blocks past K are zero with scale 2^0.
 //
@@ -258,7 +78,7 @@ __device__ __forceinline__ float act_to_f32(uint16_t v, bool is_bf16) {
 // wait counter is concerned, so activation loads issued behind a chip-wide
 // weight prefetch would wait for all of it.
 template <int NT, bool kGather, typename F, typename G>
-__device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __restrict__ sorted,
+__device__ void stage_split(const void* __restrict__ src, const int32_t* __restrict__ sorted,
                             int row0, int nvalid, int k, int K, uint8_t* lds, int* s_row,
                             F&& after_loads, G&& after_convert) {
     if (threadIdx.x < 16)
@@ -268,24 +88,41 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
     const int nblk = K / 32, nss = (nblk + 3) / 4;
     uint8_t* scales = lds + (size_t)nss * NT * 64 * 32;
     const int ntask = nvalid * nblk;
-    auto load_task = [&](int task, u32x4_t (&raw)[4]) {
+    // 16-byte loads per 32-element block: bf16 x 4, fp32 h 8
+    constexpr int kRaw = kGather ? 4 : 8;
+    auto load_task = [&](int task, u32x4_t (&raw)[kRaw]) {
         const int m = task % nvalid, blk = task / nvalid;
-        const uint16_t* p = src + (int64_t)s_row[m] * K + blk * 32;
+        const uint8_t* p = static_cast<const uint8_t*>(src) +
+                           ((int64_t)s_row[m] * K + blk * 32) * (kGather ? 2 : 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4_t*>(p + c * 8);
+        for (int c = 0; c < kRaw; ++c) raw[c] = *reinterpret_cast<const u32x4_t*>(p + 16 * c);
     };
     // Hardware K of element n of block gq is 32 gq + n: lanes 16 * (2 (gq & 1) + n / 16)
     // + m, byte 16 (gq >> 1) + n % 16.
-    auto convert_task = [&](int task, const u32x4_t (&raw)[4]) {
+    auto convert_task = [&](int task, const u32x4_t (&raw)[kRaw]) {
         const int m = task % nvalid, blk = task / nvalid;
         const int ss = blk >> 2, gq = blk & 3;
         float v[32];
+        if constexpr (kGather) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < kRaw; ++c) {
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                v[c * 8 + 2 * h] = act_to_f32((uint16_t)(raw[c][h] & 0xFFFFu), kGather);
-                v[c * 8 + 2 * h + 1] = act_to_f32((uint16_t)(raw[c][h] >> 16), kGather);
+                for (int h = 0; h < 4; ++h) {
+                    v[c * 8 + 2 * h] = bf16_to_f32(raw[c][h] & 0xFFFFu);
+                    v[c * 8 + 2 * h + 1] = bf16_to_f32(raw[c][h] >> 16);
+                }
+            }
+        } else {
+            // (the whole vector is reinterpreted: hipcc miscompiles a
+            // bit_cast of a single element of a uint32 vector to float, keeping
+            // only part of each load)
+#pragma unroll
+            for (int c = 0; c < kRaw; ++c) {
+                const f32x4_t r = __builtin_bit_cast(f32x4_t, raw[c]);
+                v[c * 4] = r[0];
+                v[c * 4 + 1] = r[1];
+                v[c * 4 + 2] = r[2];
+                v[c * 4 + 3] = r[3];
             }
         }
 #pragma unroll
@@ -312,7 +149,7 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
             scales[(ss * NT + t) * 64 + gq * 16 + m] = (uint8_t)(se + 127);
         }
     };
-    u32x4_t first[4];
+    u32x4_t first[kRaw];
     const int task0 = threadIdx.x;
     load_task(task0 < ntask ? task0 : ntask - 1, first);   // unconditional: see after_loads
     // keeps the caller's loads behind these (and in this loop iteration)
@@ -344,7 +181,7 @@ __device__ void stage_split(const uint16_t* __restrict__ src, const int32_t* __r
     if (task0 < ntask) convert_task(task0, first);
     after_convert();
     for (int task = task0 + blockDim.x; task < ntask; task += blockDim.x) {
-        u32x4_t raw[4];
+        u32x4_t raw[kRaw];
         load_task(task, raw);
         convert_task(task, raw);
     }
@@ -450,7 +287,7 @@ __device__ __forceinline__ void compute_batch(const WBatch<NB>& B, int ss0, int 
 }
 
 // kGateUp: A = [gate rows; up rows] of W13 (NS = 2), B = x rows (2 fp8 terms),
-//          epilogue h = silu(g) * u -> fp16.
+//          epilogue h = silu(g) * u -> fp32.
 // else:    A = W2 rows (NS = 1), B = h rows (3 fp8 terms), epilogue y -> fp32.
 //
 // A wavefront streams one weight row range at a time: for each of its tiles
@@ -466,10 +303,10 @@ __device__ __forceinline__ void compute_batch(const WBatch<NB>& B, int ss0, int 
 // one group); blocks of experts without pairs exit before loading anything.
 template <bool kGateUp, bool kPacked>
 __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
-    const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
+    const void* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted, int D, int F, int E, int k, int bpe,
-    void* __restrict__ out) {
+    float* __restrict__ out) {
     constexpr int NS = kGateUp ? 2 : 1;      // row streams per tile, taken in turn
     constexpr int NT = kGateUp ? 2 : 3;
     constexpr int NB = kGateUp ? 8 : 4;      // super-steps per load batch
@@ -552,15 +389,14 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
         // for its write too (measured: 1.5 us per launch at 3 tiles per
         // wave).  Further tiles (many tiles per wave, when blocks per expert
         // are few) are stored as soon as they are computed.
-        typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
-        typedef typename std::conditional<kGateUp, f16x4_t, f32x4_t>::type OutT;
-        OutT obuf[kMaxWaveTiles];
+        f32x4_t obuf[kMaxWaveTiles];
+        const int ostride = kGateUp ? F : D;
         auto epilogue = [&](int s) {
             const int j = s / seg;
-            OutT res;
+            f32x4_t res;
             if constexpr (kGateUp) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) res[q] = (_Float16)(silu_f32(acc_gate[q]) * acc[q]);
+                for (int q = 0; q < 4; ++q) res[q] = silu_f32(acc_gate[q]) * acc[q];
             } else {
                 res = acc;
             }
@@ -570,12 +406,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
                     if (jj == j) obuf[jj] = res;
             } else if (m < nvalid) {
                 const int tile = a + wave + j * kStreamWaves;
-                if constexpr (kGateUp)
-                    *reinterpret_cast<OutT*>(static_cast<_Float16*>(out) + (size_t)(row0 + m) * F +
-                                             tile * 16 + 4 * g) = res;
-                else
-                    *reinterpret_cast<OutT*>(static_cast<float*>(out) + (size_t)(row0 + m) * D +
-                                             tile * 16 + 4 * g) = res;
+                *reinterpret_cast<f32x4_t*>(out + (size_t)(row0 + m) * ostride + tile * 16 + 4 * g) = res;
             }
         };
         auto consume = [&](const WBatch<NB>& W, int s) {
@@ -613,12 +444,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void expert_stream_kernel(
             for (int jj = 0; jj < kMaxWaveTiles; ++jj) {
                 if (jj < my_tiles) {
                     const int tile = a + wave + jj * kStreamWaves;
-                    if constexpr (kGateUp)
-                        *reinterpret_cast<OutT*>(static_cast<_Float16*>(out) + (size_t)(row0 + m) * F +
-                                                 tile * 16 + 4 * g) = obuf[jj];
-                    else
-                        *reinterpret_cast<OutT*>(static_cast<float*>(out) + (size_t)(row0 + m) * D +
-                                                 tile * 16 + 4 * g) = obuf[jj];
+                    *reinterpret_cast<f32x4_t*>(out + (size_t)(row0 + m) * ostride + tile * 16 + 4 * g) =
+                        obuf[jj];
                 }
             }
         }
@@ -682,28 +509,32 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     // (the grouped GEMM addresses its buffers with 32-bit byte offsets)
     const size_t k4G = (size_t)1 << 32;
     p.gemm_ok = D % 64 == 0 && F % 64 == 0 && D <= kGemmMaxContraction &&
-                F <= kGemmMaxContraction && gemm_lds_bytes(D, true, 1, 4) <= kGemmMaxLds &&
-                gemm_lds_bytes(F, false, 1, 4) <= kGemmMaxLds && gemm_term_bytes(T, D, 2) < k4G &&
-                P * F * sizeof(_Float16) < k4G && (size_t)E * F * D < k4G;
-    // Weight streaming reads every touched expert's weights once per 16 of its
-    // pairs; the grouped GEMM stages 128-pair tiles.  Switch once the average
-    // expert receives 32 pairs.
-    p.gemm_auto = p.gemm_ok && P >= (size_t)32 * E;
+                F <= kGemmMaxContraction && gemm_lds_bytes(D, true) <= kGemmMaxLds &&
+                gemm_lds_bytes(F, false) <= kGemmMaxLds && gemm_term_bytes(T, D) < k4G &&
+                gemm_term_bytes((int)std::min(P, (size_t)1 << 30), F) < k4G &&
+                (size_t)E * F * D < k4G;
     p.stream_ok = stream_lds_bytes(D, 2, 2) <= kMaxStreamLds &&
                   stream_lds_bytes(F, 3, 1) <= kMaxStreamLds && D <= 4096 && F <= 4096;
+    // Weight streaming reads every touched expert's weights once per 16 of its
+    // pairs; the grouped GEMM stages 128-pair tiles.  Switch once the average
+    // expert receives 32 pairs, or when the streaming kernels cannot take the
+    // shape.
+    p.gemm_auto = p.gemm_ok && (P >= (size_t)32 * E || !p.stream_ok);
     p.packed_ok = p.gemm_ok && p.stream_ok;
     p.max_tiles = gemm_max_tiles(T, E, k);
     p.off_y = 0;
-    const size_t scratch = align256(P * D * sizeof(float));
-    p.off_h = scratch;                         // h [P, F] fp16, both algorithms
-    const size_t h_end = align256(p.off_h + P * F * sizeof(_Float16));
-    size_t gemm_end = h_end;
+    // h: fp32 [P, F] for the streaming kernels, fp6 term rows for the grouped
+    // GEMM; one region sized for either
+    p.off_h = align256(P * D * sizeof(float));
+    size_t h_bytes = P * F * sizeof(float);
+    if (p.gemm_ok) h_bytes = std::max(h_bytes, gemm_term_bytes((int)P, F));
+    size_t end = align256(p.off_h + h_bytes);
     if (p.gemm_ok) {
-        p.off_xq = h_end;
-        p.off_tiles = align256(p.off_xq + gemm_term_bytes(T, D, 2));
-        gemm_end = align256(p.off_tiles + sizeof(int32_t) * (2 * (size_t)p.max_tiles + 1));
+        p.off_xq = end;
+        p.off_tiles = align256(p.off_xq + gemm_term_bytes(T, D));
+        end = align256(p.off_tiles + sizeof(int32_t) * (2 * (size_t)p.max_tiles + 1));
     }
-    p.ws_bytes = gemm_end;
+    p.ws_bytes = end;
     return p;
 }
 
@@ -718,12 +549,6 @@ static int stream_blocks_per_expert(int E, int ntiles) {
     return bpe < 1 ? 1 : bpe;
 }
 
-static int blocks_per_expert(int E, int ntiles) {
-    int bpe = (2048 + E - 1) / E;
-    if (bpe > ntiles) bpe = ntiles;
-    return bpe < 1 ? 1 : bpe;
-}
-
 static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
                                  const int32_t* pos, uint16_t* out, hipEvent_t* events,
                                  hipStream_t stream);
@@ -733,7 +558,7 @@ static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* 
 template <bool kGateUp, bool kPacked>
 static hipError_t launch_stream(const MlpPlan& p, const void* act, const uint8_t* wq,
                                 const uint8_t* ws_, const int32_t* offsets,
-                                const int32_t* sorted, void* out, hipStream_t stream) {
+                                const int32_t* sorted, float* out, hipStream_t stream) {
     const size_t lds = kGateUp ? stream_lds_bytes(p.D, 2, 2) : stream_lds_bytes(p.F, 3, 1);
     const int bpe = stream_blocks_per_expert(p.E, (kGateUp ? p.F : p.D) / 16);
     if (lds > 65536) {
@@ -743,9 +568,8 @@ static hipError_t launch_stream(const MlpPlan& p, const void* act, const uint8_t
         if (er != hipSuccess) return er;
     }
     hipLaunchKernelGGL((expert_stream_kernel<kGateUp, kPacked>), dim3(p.E * bpe),
-                       dim3(kStreamWaves * 64), lds, stream,
-                       reinterpret_cast<const uint16_t*>(act), wq, ws_, offsets, sorted, p.D,
-                       p.F, p.E, p.k, bpe, out);
+                       dim3(kStreamWaves * 64), lds, stream, act, wq, ws_, offsets, sorted,
+                       p.D, p.F, p.E, p.k, bpe, out);
     return hipSuccess;
 }
 
@@ -755,43 +579,29 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
                       const int32_t* sorted, const int32_t* pos, uint16_t* out, void* ws,
                       hipEvent_t* events, hipStream_t stream) {
     char* base = static_cast<char*>(ws);
-    _Float16* h = reinterpret_cast<_Float16*>(base + p.off_h);
     float* y = reinterpret_cast<float*>(base + p.off_y);
-    const bool gemm = algo == 2 || (algo == 0 && p.gemm_auto);
-    if (gemm) {
+    if (algo == 2 || (algo == 0 && p.gemm_auto)) {
         const hipError_t er = launch_mlp_gemm(p, packed, x, w13q, w13s, w2q, w2s, offsets, sorted,
                                               y, base, events, stream);
         if (er != hipSuccess) return er;
         return launch_combine(p, y, topk_w, pos, out, events, stream);
     }
+    float* h = reinterpret_cast<float*>(base + p.off_h);
     if (events) {
         const hipError_t er = hipEventRecord(events[0], stream);
         if (er != hipSuccess) return er;
     }
-    if (p.stream_ok) {
-        hipError_t er = packed
-            ? launch_stream<true, true>(p, x, w13q, w13s, offsets, sorted, h, stream)
-            : launch_stream<true, false>(p, x, w13q, w13s, offsets, sorted, h, stream);
+    hipError_t er = packed
+        ? launch_stream<true, true>(p, x, w13q, w13s, offsets, sorted, h, stream)
+        : launch_stream<true, false>(p, x, w13q, w13s, offsets, sorted, h, stream);
+    if (er != hipSuccess) return er;
+    if (events) {
+        er = hipEventRecord(events[1], stream);
         if (er != hipSuccess) return er;
-        if (events) {
-            er = hipEventRecord(events[1], stream);
-            if (er != hipSuccess) return er;
-        }
-        er = packed ? launch_stream<false, true>(p, h, w2q, w2s, offsets, sorted, y, stream)
-                    : launch_stream<false, false>(p, h, w2q, w2s, offsets, sorted, y, stream);
-        if (er != hipSuccess) return er;
-    } else {
-        const int bpe1 = blocks_per_expert(p.E, p.F / 16);
-        hipLaunchKernelGGL(gateup_stream_kernel, dim3(p.E * bpe1), dim3(256), 0, stream, x, w13q,
-                           w13s, offsets, sorted, p.D, p.F, p.k, bpe1, h);
-        if (events) {
-            const hipError_t er = hipEventRecord(events[1], stream);
-            if (er != hipSuccess) return er;
-        }
-        const int bpe2 = blocks_per_expert(p.E, p.D / 16);
-        hipLaunchKernelGGL(down_stream_kernel, dim3(p.E * bpe2), dim3(256), 0, stream, h, w2q,
-                           w2s, offsets, p.D, p.F, bpe2, y);
     }
+    er = packed ? launch_stream<false, true>(p, h, w2q, w2s, offsets, sorted, y, stream)
+                : launch_stream<false, false>(p, h, w2q, w2s, offsets, sorted, y, stream);
+    if (er != hipSuccess) return er;
     return launch_combine(p, y, topk_w, pos, out, events, stream);
 }
 

@@ -28,23 +28,25 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
                         int32_t* sorted, int32_t* pos, float* logits_out, void* ws,
                         hipStream_t stream);
 
-// Workspace of moe_expert_mlp: y (fp32 [P, D], both paths) followed by the
-// scratch of whichever path runs (the two share one region).
+// Workspace of moe_expert_mlp: y (fp32 [P, D], both paths), h (fp32 [P, F]
+// for weight streaming, fp6 term rows for the grouped GEMM: one region),
+// then the grouped GEMM's x term rows and tile table.
 struct MlpPlan {
     int T, D, F, E, k;
-    bool gemm_ok;        // grouped-GEMM path possible: D % 64 == 0 and F % 64 == 0
+    bool gemm_ok;        // grouped-GEMM path possible (D, F % 64 == 0, LDS, 32-bit offsets)
     bool gemm_auto;      // grouped-GEMM path chosen when the caller leaves it open
     bool stream_ok;      // the streaming kernels take the shape (their LDS budget)
     bool packed_ok;      // packed weights accepted: both algorithms take the shape
     int max_tiles;       // upper bound of 128-pair tiles over all experts
     size_t off_y;
-    size_t off_h;                                    // h fp16 [P, F]
+    size_t off_h;
     size_t off_xq, off_tiles;                        // grouped GEMM: x terms, tile table
     size_t ws_bytes;
 };
 MlpPlan plan_mlp(int T, int D, int F, int E, int k);
-// algo: 0 = automatic, 1 = weight streaming, 2 = grouped GEMM (requires gemm_ok);
-// packed: w13q and w2q in the mxfp4_pack layout (requires packed_ok)
+// algo: 0 = automatic, 1 = weight streaming (requires stream_ok), 2 = grouped
+// GEMM (requires gemm_ok); packed: w13q and w2q in the mxfp4_pack layout
+// (requires packed_ok)
 hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x, const uint8_t* w13q,
                       const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
                       const float* topk_w, const int32_t* offsets, const int32_t* sorted,
@@ -53,8 +55,8 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
 
 // grouped-GEMM path (expert_gemm.hip)
 int gemm_max_tiles(int T, int E, int k);
-size_t gemm_term_bytes(int rows, int K, int NT);
-size_t gemm_lds_bytes(int K, bool gate_up, int stage, int wr);
+size_t gemm_term_bytes(int rows, int K);
+size_t gemm_lds_bytes(int K, bool gate_up);
 constexpr size_t kGemmMaxLds = 157 * 1024;    // of 160 KiB; the rest is static LDS
 constexpr int kGemmMaxContraction = 8192;      // D and F limit of the grouped GEMM
 hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, const uint8_t* w13q,

@@ -1,6 +1,7 @@
 """The C ABI library loads, exports every symbol the header declares, and
 rejects bad arguments before enqueuing anything (no GPU needed: every call
-here fails validation on the host)."""
+here fails validation on the host, or -- on a host without a gfx950 -- the
+device check that follows it)."""
 
 import ctypes
 import os
@@ -13,7 +14,7 @@ import mxfp4_quantized_mixture_amd as moe
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
 
-OK, NULL, SHAPE, WS, ENUM, HIP, ALIGN = range(7)
+OK, NULL, SHAPE, WS, ENUM, HIP, DEVICE, ALIGN = range(8)
 
 
 @pytest.fixture(scope="module")
@@ -51,9 +52,22 @@ def test_no_internal_symbols_exported():
 
 def test_status_strings(L):
     assert L.moe_status_string(OK) == b"ok"
-    for s in range(1, 7):
+    names = set()
+    for s in range(1, 8):
         assert L.moe_status_string(s) and L.moe_status_string(s) != b"ok"
-    assert L.moe_abi_version() == 1
+        names.add(L.moe_status_string(s))
+    assert len(names) == 7
+    assert b"gfx950" in L.moe_status_string(DEVICE)
+    assert L.moe_status_string(99) == b"unknown status"
+    assert L.moe_abi_version() == 2 == moe.ABI_VERSION
+
+
+def test_header_status_codes_match():
+    text = open(HEADER).read()
+    for name, code in (("MOE_OK", OK), ("MOE_ERR_NULL", NULL), ("MOE_ERR_SHAPE", SHAPE),
+                       ("MOE_ERR_WORKSPACE", WS), ("MOE_ERR_ENUM", ENUM), ("MOE_ERR_HIP", HIP),
+                       ("MOE_ERR_DEVICE", DEVICE), ("MOE_ERR_ALIGN", ALIGN)):
+        assert re.search(r"\b%s = %d\b" % (name, code), text), name
 
 
 def test_workspace_sizes(L):
@@ -71,20 +85,19 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 
 
 def test_quantize_validation(L):
-    assert L.mxfp4_quantize(FAKE, 4, 48, 0, FAKE, FAKE, None) == SHAPE
-    assert L.mxfp4_quantize(FAKE, -1, 64, 0, FAKE, FAKE, None) == SHAPE
-    assert L.mxfp4_quantize(FAKE, 4, 64, 3, FAKE, FAKE, None) == ENUM
-    L.mxfp4_quantize_ex.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
-                                    ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
-                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    assert L.mxfp4_quantize_ex(FAKE, 4, 64, 2, 2, 0, FAKE, FAKE, None) == ENUM   # rounding
-    assert L.mxfp4_quantize_ex(FAKE, 4, 64, 3, 1, 0, FAKE, FAKE, None) == ENUM   # rule
-    assert L.mxfp4_quantize_ex(FAKE, 4, 48, 2, 1, 0, FAKE, FAKE, None) == SHAPE
-    assert L.mxfp4_quantize_ex(None, 4, 64, 2, 1, 0, FAKE, FAKE, None) == NULL
-    assert L.mxfp4_quantize_ex(None, 0, 64, 2, 1, 0, None, None, None) == OK
-    assert L.mxfp4_quantize(None, 4, 64, 0, FAKE, FAKE, None) == NULL
-    assert L.mxfp4_quantize(FAKE + 2, 4, 64, 0, FAKE, FAKE, None) == ALIGN
-    assert L.mxfp4_quantize(None, 0, 64, 0, None, None, None) == OK    # empty: nothing to do
+    # mxfp4_quantize(w, rows, K, q, s, scale_rule, stream)
+    assert L.mxfp4_quantize(FAKE, 4, 48, FAKE, FAKE, 0, None) == SHAPE
+    assert L.mxfp4_quantize(FAKE, -1, 64, FAKE, FAKE, 0, None) == SHAPE
+    assert L.mxfp4_quantize(FAKE, 4, 64, FAKE, FAKE, 3, None) == ENUM
+    # mxfp4_quantize_ex(w, rows, K, q, s, scale_rule, rounding, seed, stream)
+    assert L.mxfp4_quantize_ex(FAKE, 4, 64, FAKE, FAKE, 2, 2, 0, None) == ENUM   # rounding
+    assert L.mxfp4_quantize_ex(FAKE, 4, 64, FAKE, FAKE, 3, 1, 0, None) == ENUM   # rule
+    assert L.mxfp4_quantize_ex(FAKE, 4, 48, FAKE, FAKE, 2, 1, 0, None) == SHAPE
+    assert L.mxfp4_quantize_ex(None, 4, 64, FAKE, FAKE, 2, 1, 0, None) == NULL
+    assert L.mxfp4_quantize_ex(None, 0, 64, None, None, 2, 1, 0, None) == OK
+    assert L.mxfp4_quantize(None, 4, 64, FAKE, FAKE, 0, None) == NULL
+    assert L.mxfp4_quantize(FAKE + 2, 4, 64, FAKE, FAKE, 0, None) == ALIGN
+    assert L.mxfp4_quantize(None, 0, 64, None, None, 0, None) == OK    # empty: nothing to do
     assert L.mxfp4_dequantize(FAKE, FAKE, 4, 40, FAKE, None) == SHAPE
     assert L.mxfp4_dequantize(FAKE, None, 4, 64, FAKE, None) == NULL
 
@@ -124,7 +137,7 @@ def _mlp(L, T=8, D=64, F=64, E=4, k=2, out=FAKE, ws_bytes=None, w13=FAKE):
     if ws_bytes is None:
         ws_bytes = L.moe_expert_mlp_workspace_size(T, D, F, E, k) or 1 << 20
     return L.moe_expert_mlp(FAKE, w13, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, D, F, E, k,
-                            out, FAKE, ws_bytes, None, None)
+                            out, FAKE, ws_bytes, None)
 
 
 def test_mlp_validation(L):
@@ -146,9 +159,12 @@ def test_mlp_algorithm_validation(L):
     assert _mlp_ex(L, -1) == ENUM
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, D=96) == SHAPE      # grouped GEMM needs D % 64
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=160) == SHAPE     # ... and F % 64
-    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=7296) == SHAPE    # down GEMM's LDS budget
-    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, D=8256) == SHAPE    # contraction limit
-    assert _mlp_ex(L, moe.MLP_STREAM, F=7296, out=None) == NULL # streaming takes any F
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, F=8256) == SHAPE    # contraction limit
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, D=8256) == SHAPE
+    assert _mlp_ex(L, moe.MLP_STREAM, F=3008) == SHAPE          # streaming kernels' LDS budget
+    assert _mlp_ex(L, moe.MLP_STREAM, D=3904) == SHAPE
+    assert _mlp_ex(L, moe.MLP_AUTO, D=4000) == SHAPE            # neither algorithm takes it
+    assert _mlp_ex(L, moe.MLP_STREAM, F=3008, out=None) == NULL # pointers are checked first
     assert _mlp_ex(L, moe.MLP_STREAM, out=None) == NULL
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM, out=None) == NULL
     P = moe.MLP_WEIGHTS_PACKED
@@ -165,9 +181,32 @@ def test_mlp_workspace_covers_both_algorithms(L):
     P = T * k
     n = L.moe_expert_mlp_workspace_size(T, D, F, E, k)
     y = 4 * P * D
-    assert n >= y + 2 * P * F                      # streaming: y + fp16 h
-    # grouped GEMM: y + fp16 h + x as 2 fp8 terms (144 bytes per 64 elements)
-    assert n >= y + 2 * P * F + T * (D // 64) * 144
+    assert n >= y + 4 * P * F                      # streaming: y + fp32 h
+    # grouped GEMM: y + h as fp6 term rows + x as fp6 term rows (160 bytes
+    # per 64 elements each)
+    assert n >= y + P * (F // 64) * 160 + T * (D // 64) * 160
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.is_available()
+
+
+# On a host without a gfx950 every call that passes validation stops at the
+# device check, before anything is enqueued (these calls would launch kernels
+# on fake pointers on a GPU host, so they run only where there is none).
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a GPU")
+def test_valid_calls_without_a_gfx950_return_device_error(L):
+    assert L.mxfp4_quantize(FAKE, 4, 64, FAKE, FAKE, 0, None) == DEVICE
+    assert L.mxfp4_quantize_ex(FAKE, 4, 64, FAKE, FAKE, 2, 1, 7, None) == DEVICE
+    assert L.mxfp4_dequantize(FAKE, FAKE, 4, 64, FAKE, None) == DEVICE
+    assert L.mxfp4_pack(FAKE, 32, 64, FAKE + 4096, None) == DEVICE
+    assert _route(L) == DEVICE
+    assert _mlp(L) == DEVICE
+    assert _mlp_ex(L, moe.MLP_GROUPED_GEMM) == DEVICE
+    assert _mlp_ex(L, moe.MLP_AUTO, D=3904) == DEVICE           # taken by the grouped GEMM
+    # argument errors still win over the device check
+    assert _mlp(L, F=40) == SHAPE
 
 
 def test_binding_refuses_cpu_tensors():
