@@ -25,7 +25,8 @@
  *  - The caller owns every buffer, including the workspace.  The library never
  *    allocates, frees or synchronises; a call only enqueues kernels on
  *    `stream` and returns.  Its only global state is a per-device cache of
- *    the device check below.  Calls that run concurrently on different
+ *    the device check below and, for moe_expert_mlp_noalloc, one fixed
+ *    device array per GPU.  Calls that run concurrently on different
  *    streams need separate workspaces.
  *  - Argument errors are detected before anything is enqueued and returned
  *    as a status; outputs are then untouched.  After the arguments, every
@@ -54,6 +55,9 @@
  * incompatible change (2: status codes and argument order of the contract,
  * stage events only in moe_expert_mlp_ex). */
 #define MOE_ABI_VERSION 2
+
+/* Size of the fixed device workspace of moe_expert_mlp_noalloc (16 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
 #ifdef __cplusplus
 extern "C" {
@@ -289,6 +293,36 @@ MOE_API moe_status_t moe_expert_mlp_ex(const uint16_t *x, const uint8_t *w13_q,
                                        int32_t F, int32_t E, int32_t k, uint16_t *out,
                                        void *ws, size_t ws_bytes, int algo,
                                        hipEvent_t *stage_events, hipStream_t stream);
+
+/*
+ * moe_expert_mlp_noalloc -- moe_expert_mlp_ex without a workspace argument
+ * and without stage events, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is instead a fixed device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; its device address is looked up on the first call on each
+ * device.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Arguments, arithmetic, preconditions and results are
+ * those of moe_expert_mlp_ex (bit-identical outputs), the caller still
+ * passes every input and the output.
+ * Limit: calls whose moe_expert_mlp_workspace_size(T, D, F, E, k) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_ERR_WORKSPACE before
+ * anything is enqueued (at D = F = 2880 and k = 4: up to T = 168 tokens).
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one GPU -- on different streams, or from different threads -- race and
+ * must be serialised by the caller.
+ * Errors: as moe_expert_mlp_ex; MOE_ERR_HIP also if the array's address
+ * cannot be obtained.
+ */
+MOE_API moe_status_t moe_expert_mlp_noalloc(const uint16_t *x, const uint8_t *w13_q,
+                                            const uint8_t *w13_s, const uint8_t *w2_q,
+                                            const uint8_t *w2_s, const float *topk_w,
+                                            const int32_t *offsets,
+                                            const int32_t *sorted_pairs,
+                                            const int32_t *pair_pos, int32_t T, int32_t D,
+                                            int32_t F, int32_t E, int32_t k, uint16_t *out,
+                                            int algo, hipStream_t stream);
 
 #ifdef __cplusplus
 }

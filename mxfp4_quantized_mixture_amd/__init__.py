@@ -14,6 +14,7 @@ Functions mirror the C entry points:
     moe_expert_mlp(x, weights, routing, algo=MLP_AUTO) -> bf16 [T, D]
       (moe_expert_mlp_ex in the C ABI when an algorithm is named or the
       weights are packed)
+    moe_expert_mlp_noalloc(x, weights, routing, out, algo=MLP_AUTO)
 and MoELayer bundles quantized weights and workspaces for repeated calls.
 """
 
@@ -26,6 +27,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "mxfp4_pack", "moe_route", "moe_expert_mlp",
+           "moe_expert_mlp_noalloc", "NOALLOC_SCRATCH_BYTES",
            "Routing", "ExpertWeights", "MoELayer", "MoEError", "lib",
            "SCALE_FLOOR_DIV6", "SCALE_OCP", "SCALE_CEIL_DIV6", "ROUND_NEAREST_EVEN",
            "ROUND_STOCHASTIC", "MLP_AUTO", "MLP_STREAM", "MLP_GROUPED_GEMM", "MLP_WEIGHTS_PACKED",
@@ -33,6 +35,7 @@ __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "mxfp4_pack", "moe_route", "moe
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
 ABI_VERSION = 2
+NOALLOC_SCRATCH_BYTES = 16 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 SCALE_FLOOR_DIV6 = 0
 SCALE_OCP = 1
 SCALE_CEIL_DIV6 = 2
@@ -89,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_mlp_ex.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                         P, P, sz, ctypes.c_int, P, P]
         L.moe_expert_mlp_ex.restype = ctypes.c_int
+        L.moe_expert_mlp_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                             P, ctypes.c_int, P]
+        L.moe_expert_mlp_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -281,6 +287,27 @@ def moe_expert_mlp(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
         _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
         _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), algo | weights.algo_flags,
         ev, _stream(x.device)))
+    return out
+
+
+def moe_expert_mlp_noalloc(x: torch.Tensor, weights: ExpertWeights, routing: Routing,
+                           out: torch.Tensor, algo: int = MLP_AUTO) -> torch.Tensor:
+    """moe_expert_mlp on the library's fixed per-GPU workspace (no workspace
+    argument; nothing is allocated, `out` must be given).  Calls that overlap
+    on one GPU race on that workspace."""
+    T, D = x.shape
+    E, F = weights.E, weights.F
+    k = routing.ids.shape[1]
+    if weights.D != D:
+        raise ValueError("expert weights do not match d_model")
+    _check("moe_expert_mlp_noalloc", lib().moe_expert_mlp_noalloc(
+        _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
+        _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
+        _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w", torch.float32),
+        _dev(routing.offsets, "offsets", torch.int32),
+        _dev(routing.sorted_pairs, "sorted_pairs", torch.int32),
+        _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
+        _dev(out, "out", torch.bfloat16), algo | weights.algo_flags, _stream(x.device)))
     return out
 
 

@@ -46,6 +46,37 @@ bool route_shape_ok(int32_t T, int32_t D, int32_t E, int32_t k) {
     return (int64_t)T * k < ((int64_t)1 << 31) && (int64_t)T * D < ((int64_t)1 << 40);
 }
 
+// ---------------------------------------------------------------------------
+// Workspace of moe_expert_mlp_noalloc: a fixed device array, one copy per
+// GPU (each device holds its own at its own address until the process ends).
+// Host code never uses the array's name as an address: the device address
+// is looked up once per device with hipGetSymbolAddress (that device
+// current) and kept in g_scratch.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device of `stream` (the current device for the null stream), or -1.
+int stream_device(hipStream_t stream) {
+    int dev = -1;
+    if (stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) return -1;
+    return dev >= 0 && dev < kMaxDevices ? dev : -1;
+}
+
+// This device's copy of `scratch`, or nullptr if its address cannot be had.
+void* scratch_on(int dev) {
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    const hipError_t er = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (er != hipSuccess) return nullptr;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,4 +207,37 @@ moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const ui
                                       stream));
 }
 
+moe_status_t moe_expert_mlp_noalloc(const uint16_t* x, const uint8_t* w13_q,
+                                    const uint8_t* w13_s, const uint8_t* w2_q,
+                                    const uint8_t* w2_s, const float* topk_w,
+                                    const int32_t* offsets, const int32_t* sorted_pairs,
+                                    const int32_t* pair_pos, int32_t T, int32_t D, int32_t F,
+                                    int32_t E, int32_t k, uint16_t* out, int algo,
+                                    hipStream_t stream) {
+    const bool packed = (algo & MOE_MLP_WEIGHTS_PACKED) != 0;
+    const int base = algo & ~MOE_MLP_WEIGHTS_PACKED;
+    if (base != MOE_MLP_AUTO && base != MOE_MLP_STREAM && base != MOE_MLP_GROUPED_GEMM)
+        return MOE_ERR_ENUM;
+    if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return MOE_ERR_SHAPE;
+    if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_w || !offsets || !sorted_pairs ||
+        !pair_pos || !out)
+        return MOE_ERR_NULL;
+    const moe::MlpPlan plan = moe::plan_mlp(T, D, F, E, k);
+    if (base == MOE_MLP_GROUPED_GEMM && !plan.gemm_ok) return MOE_ERR_SHAPE;
+    if (base == MOE_MLP_STREAM && !plan.stream_ok) return MOE_ERR_SHAPE;
+    if (base == MOE_MLP_AUTO && !plan.stream_ok && !plan.gemm_ok) return MOE_ERR_SHAPE;
+    if (packed && !plan.packed_ok) return MOE_ERR_SHAPE;
+    if (plan.ws_bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
+        !aligned16(w2_s) || !aligned16(out))
+        return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
+    const int dev = stream_device(stream);
+    void* ws = dev < 0 ? nullptr : scratch_on(dev);
+    if (!ws) return MOE_ERR_HIP;
+    return hip_status(moe::launch_mlp(plan, base, packed, x, w13_q, w13_s, w2_q, w2_s, topk_w,
+                                      offsets, sorted_pairs, pair_pos, out, ws, nullptr, stream));
+}
+
 }  // extern "C"
+
