@@ -4,20 +4,27 @@
 
 A step is one pass of the whole layer -- moe_route then moe_expert_mlp --
 over one batch of synthetic tokens already resident in HBM.  The default
-workload is the GPT-OSS-20B-shaped decode step (T=32 tokens, d_model = d_ff =
-2880, 32 experts, top-4).  Expert weights are quantized to MXFP4 once,
-outside the timed region, and NCOPIES copies are rotated step to step so the
-256 MB last-level cache cannot hold the weights between steps.
+(headline) workload is the GPT-OSS-120B-shaped prefill with Zipf-biased
+routing: T = 16384 tokens, d_model = d_ff = 2880, 128 experts, top-4, the
+largest configuration of the benchmark set.  Expert weights are quantized to
+MXFP4 once, outside the timed region (packed for the expert kernels), and
+NCOPIES copies are rotated step to step so the 256 MB last-level cache cannot
+hold them between steps.
 
-Prints one JSON line.  `value` is tokens/s of the whole layer; `roofline`
-prices the dominant kernel (the gate/up expert kernel) using algorithmic
-bytes / flops and the kernel's own duration from HIP events recorded on its
-stream in the timed region: against HBM bandwidth when the layer streams
-the expert weights (few pairs per expert), against the matrix cores' fp8
-rate when it runs the grouped GEMM (the block-scaled fp4 x fp8 products
-issue at the fp8 rate).  `cpu_baseline` is the single-threaded CPU oracle on
-the same workload (the whole decode step, or a token sample for prefill
-workloads).
+Prints one JSON line.  `value` is tokens/s of the whole layer over K timed
+steps.  `roofline` prices the dominant kernel (the gate/up expert kernel)
+with its algorithmic work -- bytes for weight streaming, 4 D F flops per
+routed pair for the grouped GEMM -- over its mean duration from HIP events
+recorded on the layer's stream, against the published MI355X peak of what it
+runs on (HBM 8 TB/s; fp4 x fp6 block-scaled matrix cores 10.1 PFLOP/s);
+`roofline_down` does the same for the down kernel.  `traffic` is the HBM
+bytes per launch from the committed rocprofv3 counter summary when it was
+taken on the current kernel source, else null.  `cpu_baseline` is the
+single-threaded fp64 CPU oracle on a bounded sample of the same workload.
+With the headline workload (and without --no-configs) the line also carries
+`configs`: the other four workloads and the headline's separately timed
+mxfp4_quantize, each with its own timing and roofline; and `probes`: the
+achievable HBM read rate and matrix-core rates measured on this GPU.
 """
 
 from __future__ import annotations
@@ -26,7 +33,7 @@ import argparse
 import hashlib
 import json
 import os
-import platform
+import subprocess
 import sys
 import time
 
@@ -36,8 +43,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix cores, TFLOP/s
+FP6_PEAK_TFLOPS = 10100.0      # MI355X dense fp6 / fp4 matrix cores, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8
+F16_PEAK_TFLOPS = 2500.0       # dense fp16 / bf16
 NCOPIES = 3
+HEADLINE = "gptoss120b_prefill_skewed"
+OTHER_CONFIGS = ["tiny", "gptoss20b_decode", "gptoss120b_decode", "gptoss20b_prefill"]
+CONFIG_STEPS, CONFIG_WARMUP = 100, 10
+ACT_TERMS = 3                  # grouped GEMM: x and h as 3 fp6 terms
 
 
 def algorithmic_work(cfg, counts: np.ndarray) -> dict:
@@ -48,10 +61,11 @@ def algorithmic_work(cfg, counts: np.ndarray) -> dict:
     w2_bytes = D * (F // 2 + F // 32)
     x_bytes = 2 * T * D
     step_bytes = touched * (w13_bytes + w2_bytes) + 4 * E * D + 4 * E + x_bytes + 2 * T * D
-    gateup_bytes = touched * w13_bytes + x_bytes
     pairs = T * k
-    return dict(touched=touched, step_bytes=step_bytes, gateup_bytes=gateup_bytes,
-                step_flops=6 * D * F * pairs, gateup_flops=4 * D * F * pairs)
+    return dict(touched=touched, step_bytes=step_bytes,
+                gateup_bytes=touched * w13_bytes + x_bytes, down_bytes=touched * w2_bytes,
+                step_flops=6 * D * F * pairs, gateup_flops=4 * D * F * pairs,
+                down_flops=2 * D * F * pairs)
 
 
 def packed_ok(cfg) -> bool:
@@ -59,6 +73,12 @@ def packed_ok(cfg) -> bool:
     algorithms: contraction sizes multiples of 64 within the streaming
     kernels' LDS budget)."""
     return cfg.D % 64 == 0 and cfg.F % 64 == 0 and cfg.D <= 3840 and cfg.F <= 2944
+
+
+def uses_grouped_gemm(cfg, algo: str) -> bool:
+    """The library's automatic choice: the grouped GEMM once the average expert
+    receives 32 pairs, weight streaming below that."""
+    return algo == "gemm" or (algo == "auto" and cfg.T * cfg.k >= 32 * cfg.E)
 
 
 def read_traffic(kernel: str, workload: str, source: str, layout: str):
@@ -83,64 +103,261 @@ def read_traffic(kernel: str, workload: str, source: str, layout: str):
         return None
 
 
-def cpu_baseline(cfg, inp, tokens) -> dict:
-    """The CPU oracle as it is (single-threaded C, fp64) on the same inputs."""
-    from oracle import oracle as orc
+def host_cpu() -> dict:
+    model = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True,
+                                   timeout=20).stdout.strip())
+    except (OSError, subprocess.SubprocessError, ValueError):
+        nproc = os.cpu_count()
+    return {"model": model, "nproc": nproc}
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int = 32) -> dict:
+    """The CPU oracle as it is (single-threaded C, fp64) on a bounded sample of
+    the same workload, in tokens/s.  Routing runs for all T tokens; the expert
+    MLP and combine for all tokens when T <= 64, else for `sample_tokens`
+    evenly spaced tokens.  The oracle decodes each expert's weights once per
+    call (a fixed cost a per expert, measured on its own) and then spends
+    about b per routed pair, so the whole-workload time is extrapolated as
+    t_route + (touched experts) a + T k b, with b taken from the sample."""
     from concurrent.futures import ThreadPoolExecutor
+    from oracle import oracle as orc
 
     x, wr, b, w13, w2 = inp
-    # oracle-side quantization is input preparation, not timed
-    with ThreadPoolExecutor(max_workers=16) as ex:
-        q13 = list(ex.map(lambda e: orc.quantize(w13[e]), range(cfg.E)))
-        q2 = list(ex.map(lambda e: orc.quantize(w2[e]), range(cfg.E)))
-    q13q = np.stack([a for a, _ in q13]); q13s = np.stack([s for _, s in q13])
-    q2q = np.stack([a for a, _ in q2]); q2s = np.stack([s for _, s in q2])
+    T, k, E = cfg.T, cfg.k, cfg.E
     t0 = time.perf_counter()
-    r = orc.route(x, wr, b, cfg.k)
-    orc.moe(x, q13q, q13s, q2q, q2s, r["ids"], r["w"], cfg.F,
-            tokens=None if tokens is None else np.asarray(tokens, np.int32))
-    dt = time.perf_counter() - t0
-    n = cfg.T if tokens is None else len(tokens)
-    what = ("whole step: %d tokens routed (router over all %d tokens), %d expert pairs, "
-            "combine" % (n, cfg.T, n * cfg.k))
-    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": what, "seconds": dt, "host_cpu": platform.processor() or platform.machine()}
+    r = orc.route(x, wr, b, k)
+    t_route = time.perf_counter() - t0
+    tokens = np.arange(T) if T <= 64 else np.arange(0, T, T // sample_tokens)[:sample_tokens]
+    used = sorted(set(r["ids"][tokens].ravel().tolist()))
+    # quantizing the weights for the oracle is input preparation: untimed
+    q13 = np.zeros((E, 2 * cfg.F, cfg.D // 2), np.uint8)
+    s13 = np.zeros((E, 2 * cfg.F, cfg.D // 32), np.uint8)
+    q2 = np.zeros((E, cfg.D, cfg.F // 2), np.uint8)
+    s2 = np.zeros((E, cfg.D, cfg.F // 32), np.uint8)
+
+    def prep(e):
+        q13[e], s13[e] = orc.quantize(w13[e])
+        q2[e], s2[e] = orc.quantize(w2[e])
+
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        list(ex.map(prep, used))
+    t0 = time.perf_counter()
+    orc.moe(x, q13, s13, q2, s2, r["ids"], r["w"], cfg.F,
+            tokens=None if T <= 64 else tokens.astype(np.int32))
+    t_moe = time.perf_counter() - t0
+    touched = int(len(np.unique(r["ids"])))
+    if T <= 64:
+        secs = t_route + t_moe
+        how = "whole workload: route, %d experts' MLPs for all %d pairs, combine" % (
+            touched, T * k)
+        sample = "all %d tokens" % T
+    else:
+        e0 = used[0]
+        t0 = time.perf_counter()
+        orc.expert_mlp(x, q13[e0], s13[e0], q2[e0], s2[e0], cfg.F, np.zeros(0, np.int32))
+        a = time.perf_counter() - t0
+        pairs = len(tokens) * k
+        bpair = max(t_moe - len(used) * a, 0.0) / pairs
+        secs = t_route + touched * a + T * k * bpair
+        how = ("route over all %d tokens (%.1f s); expert MLP + combine for %d tokens "
+               "(%d pairs on %d experts, %.1f s); per-expert weight decode a = %.2f s, per "
+               "pair b = %.1f ms; whole workload = route + %d a + %d b" %
+               (T, t_route, len(tokens), pairs, len(used), t_moe, a, bpair * 1e3, touched,
+                T * k))
+        sample = "every %d-th token: %d of %d" % (T // sample_tokens, len(tokens), T)
+    return {"value": T / secs, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "method": how, "seconds_measured": t_route + t_moe,
+            "seconds_whole_workload": secs, "host_cpu": host_cpu()}
 
 
-def bench_quantize(cfg, args, moe, torch, dev) -> int:
-    """mxfp4_quantize of all the workload's expert weights, W13 [E*2F, D] and
-    W2 [E*D, F] bf16 (one call each per step), both roundings; HBM bytes =
-    2 B read per element + 0.5 + 1/32 B written."""
+def bf16_dev(torch, dev, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def run_layer(cfg, steps, warmup, seed, algo, layout, moe, torch, dev, keep_inputs=False):
+    """Quantize, time `steps` layer steps (value region, then a second region
+    with per-stage events) and return timings plus what the rooflines need."""
     from synth import moe_inputs as MI
-    w13, w2 = MI.gen_experts(cfg, args.seed, threads=16)
-    mats = [torch.from_numpy(a.reshape(-1, a.shape[-1]).view(np.int16)).to(dev).view(torch.bfloat16)
-            for a in (w13, w2)]
-    del w13, w2
+
+    wr, b = MI.gen_router(cfg, seed)
+    x = MI.gen_x(cfg, seed)
+    w13, w2 = MI.gen_experts(cfg, seed, threads=16)
+    xd, wrd, bd = bf16_dev(torch, dev, x), torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)
+    packed = layout == "packed" or (layout == "auto" and packed_ok(cfg))
+    w13d, w2d = bf16_dev(torch, dev, w13), bf16_dev(torch, dev, w2)
+    base = moe.ExpertWeights.quantize(w13d, w2d, packed=packed)
+    if not keep_inputs:
+        del w13d, w2d
+    copies = [base] + [moe.ExpertWeights(base.w13_q.clone(), base.w13_s.clone(),
+                                         base.w2_q.clone(), base.w2_s.clone(), packed)
+                       for _ in range(NCOPIES - 1)]
+    out = torch.empty(cfg.T, cfg.D, dtype=torch.bfloat16, device=dev)
+    routing = moe.alloc_routing(cfg.T, cfg.E, cfg.k, dev)
+    route_ws = moe.route_workspace(cfg.T, cfg.D, cfg.E, cfg.k, dev)
+    mlp_ws = moe.mlp_workspace(cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, dev)
+    algo_id = {"auto": moe.MLP_AUTO, "stream": moe.MLP_STREAM, "gemm": moe.MLP_GROUPED_GEMM}[algo]
+    layers = [moe.PreparedLayer(xd, wrd, bd, w, cfg.k, out, routing, route_ws, mlp_ws, algo=algo_id)
+              for w in copies]
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        layers[i % NCOPIES]()
+    # Timed region 1 (value): the layer alone, nothing else on the stream.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        layers[i % NCOPIES]()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # Timed region 2 (per-kernel durations): the same steps with HIP events
+    # recorded on the layer's stream around each expert kernel.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evarr = [moe.PreparedLayer.event_array(e) for e in ev]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        layers[i % NCOPIES](evarr[i])
+    torch.cuda.synchronize()
+    stage = {"gate_up": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+             "down": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+             "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))}
+    res = dict(ms_per_step=total_ms / steps, stage_ms=stage, counts=routing.counts.cpu().numpy(),
+               packed=packed, gemm=uses_grouped_gemm(cfg, algo))
+    if keep_inputs:
+        res["inputs"] = (x, wr, b, w13, w2)
+        res["bf16_weights"] = (w13d, w2d)
+    del layers, copies, base, mlp_ws, route_ws
+    torch.cuda.synchronize()
+    return res
+
+
+def rooflines(cfg, run) -> tuple[dict, dict, dict]:
+    """(gate/up kernel, down kernel, whole layer) rooflines."""
+    work = algorithmic_work(cfg, run["counts"])
+    st, gemm, packed = run["stage_ms"], run["gemm"], run["packed"]
+    layout = "packed" if packed else "row-major"
+    kinds = ",packed" if packed else ""
+    if not gemm:
+        def hbm(bytes_, ms, kernel, traffic):
+            a = bytes_ / (ms * 1e-3) / 1e9
+            return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": a / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
+                    "algorithmic_per_launch": bytes_, "avg_launch_ms": ms}
+        gu = hbm(work["gateup_bytes"], st["gate_up"], "expert_stream_kernel<gate_up%s>" % kinds,
+                 read_traffic("gateup", cfg.name, "expert_mlp.hip", layout))
+        dn = hbm(work["down_bytes"], st["down"], "expert_stream_kernel<down%s>" % kinds,
+                 read_traffic("down", cfg.name, "expert_mlp.hip", layout))
+        a = work["step_bytes"] / (run["ms_per_step"] * 1e-3) / 1e9
+        layer = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": a / HBM_PEAK_GBS}
+    else:
+        def mfma(flops, ms, kernel, traffic):
+            a = flops / (ms * 1e-3) / 1e12
+            # the activations enter as ACT_TERMS fp6 terms: the matrix cores
+            # execute ACT_TERMS times the algorithmic flops
+            return {"bound": "mfma", "achieved": a, "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": a / FP6_PEAK_TFLOPS, "traffic": traffic, "kernel": kernel,
+                    "algorithmic_per_launch": flops, "avg_launch_ms": ms,
+                    "operand_types": "fp4 (E2M1) weights x fp6 (E2M3) activation terms",
+                    "executed_tflops": ACT_TERMS * a,
+                    "executed_frac": ACT_TERMS * a / FP6_PEAK_TFLOPS}
+        gu = mfma(work["gateup_flops"], st["gate_up"], "expert_gemm_kernel<gate_up%s>" % kinds,
+                  read_traffic("gateup_gemm", cfg.name, "expert_gemm.hip", layout))
+        dn = mfma(work["down_flops"], st["down"], "expert_gemm_kernel<down%s>" % kinds,
+                  read_traffic("down_gemm", cfg.name, "expert_gemm.hip", layout))
+        a = work["step_flops"] / (run["ms_per_step"] * 1e-3) / 1e12
+        layer = {"bound": "mfma", "achieved": a, "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": a / FP6_PEAK_TFLOPS, "executed_frac": ACT_TERMS * a / FP6_PEAK_TFLOPS}
+    layer["touched_experts"] = work["touched"]
+    return gu, dn, layer
+
+
+def quantize_timing(mats, steps, moe, torch) -> dict:
+    """mxfp4_quantize of the given bf16 matrices (one call each per step),
+    nearest-even and stochastic rounding; HBM bytes = 2 B read per element +
+    0.5 + 1/32 B written."""
     elems = sum(m.numel() for m in mats)
     nbytes = elems * 2 + elems // 2 + elems // 32
-    out = {}
+    out = {"bytes_per_step": nbytes, "matrices": [list(m.shape) for m in mats]}
     for name, kw in (("nearest_even", {}), ("stochastic", {"stochastic": True, "seed": 1})):
         rule = moe.SCALE_CEIL_DIV6 if kw else moe.SCALE_FLOOR_DIV6
-        for _ in range(max(args.warmup // 10, 2)):
+        for _ in range(2):
             for m in mats:
                 moe.mxfp4_quantize(m, rule, **kw)
-        n = max(args.steps // 20, 5)
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
-        for _ in range(n):
+        for _ in range(steps):
             for m in mats:
                 moe.mxfp4_quantize(m, rule, **kw)
         stop.record()
         torch.cuda.synchronize()
-        ms = start.elapsed_time(stop) / n
-        out[name] = {"ms": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9,
-                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    print(json.dumps({"metric": "mxfp4_quantize HBM GB/s",
-                      "workload": "%s: all %d experts' W13 and W2" % (cfg.name, cfg.E),
-                      "matrices": [list(m.shape) for m in mats], "bytes_per_step": nbytes,
-                      "steps": n, "results": out}), flush=True)
-    return 0
+        ms = start.elapsed_time(stop) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "achieved_GBs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+                     "steps": steps}
+    return out
+
+
+def probes(torch, dev) -> dict:
+    """Achievable ceilings on this GPU (libmoe_probe.so): one streaming read of
+    a 4 GiB buffer (far beyond the 256 MB last-level cache), and 8 independent
+    32x32 matrix-core chains per wavefront for each operand type."""
+    import ctypes
+
+    from mxfp4_quantized_mixture_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise ImportError("%s is not built (python -m mxfp4_quantized_mixture_amd.build)"
+                          % B.PROBE_LIB)
+    L = ctypes.CDLL(B.PROBE_LIB)
+    P = ctypes.c_void_p
+    L.moe_probe_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, P]
+    L.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    L.moe_probe_mfma_flops.argtypes = [ctypes.c_int]
+    L.moe_probe_mfma_flops.restype = ctypes.c_double
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    res = {}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    for blocks in (2048, 8192):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            assert L.moe_probe_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream) == 0
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(5):
+            L.moe_probe_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream)
+        stop.record()
+        torch.cuda.synchronize()
+        res["hbm_read_GBs_%d_blocks" % blocks] = 5 * nbytes / (start.elapsed_time(stop) * 1e-3) / 1e9
+    del buf
+    names = {0: "fp4_fp4", 1: "fp4_fp6", 2: "fp4_fp8", 3: "fp8_fp8", 4: "f16", 5: "bf16"}
+    blocks, iters = 2048, 500
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for kind, name in names.items():
+        assert L.moe_probe_mfma(kind, blocks, 10, sink.data_ptr(), stream) == 0
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        L.moe_probe_mfma(kind, blocks, iters, sink.data_ptr(), stream)
+        stop.record()
+        torch.cuda.synchronize()
+        flops = blocks * 4 * 8 * iters * L.moe_probe_mfma_flops(kind)
+        res["mfma_TFLOPs_" + name] = flops / (start.elapsed_time(stop) * 1e-3) / 1e12
+    res["published_peaks"] = {"hbm_GBs": HBM_PEAK_GBS, "fp4_fp6_TFLOPs": FP6_PEAK_TFLOPS,
+                              "fp8_TFLOPs": FP8_PEAK_TFLOPS, "f16_bf16_TFLOPs": F16_PEAK_TFLOPS}
+    return res
 
 
 def main() -> int:
@@ -148,16 +365,20 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gptoss20b_decode")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="only the named workload: no per-config results, quantize timing or probes")
     ap.add_argument("--algo", default="auto", choices=["auto", "stream", "gemm"],
                     help="expert algorithm (default: the library's automatic choice)")
     ap.add_argument("--layout", default="auto", choices=["auto", "canonical", "packed"],
                     help="expert weight code layout (default: packed where the kernels take it)")
     ap.add_argument("--quantize", action="store_true",
-                    help="time mxfp4_quantize (nearest-even and stochastic rounding) on the "
-                         "workload's expert weights (W13 and W2) instead of the layer")
+                    help="only time mxfp4_quantize (nearest-even and stochastic rounding) on the "
+                         "workload's expert weights (W13 and W2)")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the achievable-peak probes (HBM read, matrix cores)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a kernel of known traffic)")
@@ -182,124 +403,78 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": nbytes, "dispatches": 5}), flush=True)
         return 0
+    if args.probes:
+        print(json.dumps({"probes": probes(torch, dev)}), flush=True)
+        return 0
     cfg = MI.CONFIGS[args.workload]
     if args.quantize:
-        return bench_quantize(cfg, args, moe, torch, dev)
-    wr, b = MI.gen_router(cfg, args.seed)
-    x = MI.gen_x(cfg, args.seed)
-    w13, w2 = MI.gen_experts(cfg, args.seed, threads=16)
+        w13, w2 = MI.gen_experts(cfg, args.seed, threads=16)
+        mats = [bf16_dev(torch, dev, a.reshape(-1, a.shape[-1])) for a in (w13, w2)]
+        q = quantize_timing(mats, max(args.steps // 20, 5), moe, torch)
+        print(json.dumps({"metric": "mxfp4_quantize HBM GB/s",
+                          "workload": "%s: all %d experts' W13 and W2" % (cfg.name, cfg.E),
+                          "results": q}), flush=True)
+        return 0
 
-    def bf16(a):
-        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    xd, wrd, bd = bf16(x), torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)
-    packed = args.layout == "packed" or (args.layout == "auto" and packed_ok(cfg))
-    layout = "packed" if packed else "row-major"
-    base = moe.ExpertWeights.quantize(bf16(w13), bf16(w2), packed=packed)
-    copies = [base] + [moe.ExpertWeights(base.w13_q.clone(), base.w13_s.clone(),
-                                         base.w2_q.clone(), base.w2_s.clone(), packed)
-                       for _ in range(NCOPIES - 1)]
-    out = torch.empty(cfg.T, cfg.D, dtype=torch.bfloat16, device=dev)
-    routing = moe.alloc_routing(cfg.T, cfg.E, cfg.k, dev)
-    route_ws = moe.route_workspace(cfg.T, cfg.D, cfg.E, cfg.k, dev)
-    mlp_ws = moe.mlp_workspace(cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, dev)
-    algo = {"auto": moe.MLP_AUTO, "stream": moe.MLP_STREAM,
-            "gemm": moe.MLP_GROUPED_GEMM}[args.algo]
-    layers = [moe.PreparedLayer(xd, wrd, bd, w, cfg.k, out, routing, route_ws, mlp_ws, algo=algo)
-              for w in copies]
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        layers[i % NCOPIES]()
-    K = args.steps
-    # Timed region 1 (value): the layer alone, nothing else on the stream.
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        layers[i % NCOPIES]()
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    # Timed region 2 (per-kernel durations): the same K steps with HIP events
-    # recorded on the layer's stream around each expert kernel.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    evarr = [moe.PreparedLayer.event_array(e) for e in ev]
-    torch.cuda.synchronize()
-    for i in range(K):
-        layers[i % NCOPIES](evarr[i])
-    torch.cuda.synchronize()
-    gateup_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    down_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    combine_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    ms_per_step = total_ms / K
-
-    counts = routing.counts.cpu().numpy()
-    work = algorithmic_work(cfg, counts)
-    # the library's automatic choice: the grouped GEMM once the average expert
-    # receives 32 pairs, weight streaming below that
-    decode = (args.algo == "stream" or
-              (args.algo == "auto" and cfg.T * cfg.k < 32 * cfg.E))
-    if decode:
-        ach = work["gateup_bytes"] / (gateup_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS}
-        layer = work["step_bytes"] / (ms_per_step * 1e-3) / 1e9
-        layer_roof = {"bound": "hbm", "achieved": layer, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": layer / HBM_PEAK_GBS}
-    else:
-        ach = work["gateup_flops"] / (gateup_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / FP8_PEAK_TFLOPS,
-                # x enters as 2 exact fp8 terms: the matrix cores execute twice the flops
-                "executed_tflops": 2 * ach}
-        layer = work["step_flops"] / (ms_per_step * 1e-3) / 1e12
-        layer_roof = {"bound": "mfma", "achieved": layer, "peak": FP8_PEAK_TFLOPS,
-                      "unit": "TFLOP/s", "frac": layer / FP8_PEAK_TFLOPS}
-    if decode:
-        roof["kernel"] = "expert_stream_kernel<gate_up%s>" % (",packed" if packed else "")
-        roof["traffic"] = read_traffic("gateup", cfg.name, "expert_mlp.hip", layout)
-    else:
-        roof["kernel"] = "expert_gemm_kernel<gate_up%s>" % (",packed" if packed else "")
-        roof["traffic"] = read_traffic("gateup_gemm", cfg.name, "expert_gemm.hip", layout)
-    roof["algorithmic_per_launch"] = work["gateup_bytes"] if decode else work["gateup_flops"]
-    roof["avg_launch_ms"] = gateup_ms
-
+    headline = args.workload == HEADLINE and not args.no_configs
+    run = run_layer(cfg, args.steps, args.warmup, args.seed, args.algo, args.layout, moe, torch,
+                    dev, keep_inputs=headline or not args.no_cpu_baseline)
+    gu, dn, layer = rooflines(cfg, run)
+    ms = run["ms_per_step"]
     result = {
         "metric": "MXFP4 MoE-layer tokens/s",
-        "value": cfg.T / (ms_per_step * 1e-3),
+        "value": cfg.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*fp8->f32" if decode else "mxfp4*fp8->f32 (gate/up), f16*f16->f32 (down)",
+        "dtype": ("mxfp4 x fp6 terms -> f32" if run["gemm"] else "mxfp4 x fp8 terms -> f32"),
         "data": "synthetic",
         "config": {"workload": cfg.description, "name": cfg.name, "tokens": cfg.T,
                    "d_model": cfg.D, "d_ff": cfg.F, "experts": cfg.E, "top_k": cfg.k,
                    "expert_weights": "mxfp4 (e2m1 + e8m0 per 32)",
-                   "matrix_cores": ("block-scaled mfma: mxfp4 weights x fp8 residual terms "
-                                    "of the activations, fp32 accumulate") if decode else
-                                   ("gate/up: block-scaled mfma, mxfp4 weights x 2 fp8 terms "
-                                    "of x; down: f16 mfma, fp16 h x W2 codes converted to "
-                                    "fp16 per tile; fp32 accumulate"),
-                   "expert_algorithm": "weight streaming" if decode else "grouped gemm",
-                   "weight_layout": "packed 32x64 fragments" if packed else "row-major",
-                   "touched_experts": work["touched"], "weight_copies_rotated": NCOPIES,
+                   "matrix_cores": ("block-scaled mfma: mxfp4 weights as stored x x and h as 3 "
+                                    "fp6 (e2m3) terms, fp32 accumulate") if run["gemm"] else
+                                   ("block-scaled mfma: mxfp4 weights as stored x x as 2 and h as "
+                                    "3 fp8 (e4m3) terms, fp32 accumulate"),
+                   "expert_algorithm": "grouped gemm" if run["gemm"] else "weight streaming",
+                   "weight_layout": "packed 32x64 fragments" if run["packed"] else "row-major",
+                   "touched_experts": layer["touched_experts"], "weight_copies_rotated": NCOPIES,
                    "parallelism": "single GPU"},
-        "roofline": roof,
-        "layer_roofline": layer_roof,
-        "stage_ms": {"gate_up": gateup_ms, "down": down_ms, "combine": combine_ms},
+        "roofline": gu,
+        "roofline_down": dn,
+        "layer_roofline": layer,
+        "stage_ms": run["stage_ms"],
     }
+    if headline:
+        w13d, w2d = run.pop("bf16_weights")
+        mats = [w13d.view(-1, w13d.shape[-1]), w2d.view(-1, w2d.shape[-1])]
+        q = quantize_timing(mats, 10, moe, torch)
+        q["workload"] = "%s: all %d experts' W13 [%d, %d] and W2 [%d, %d] bf16" % (
+            cfg.name, cfg.E, cfg.E * 2 * cfg.F, cfg.D, cfg.E * cfg.D, cfg.F)
+        del mats, w13d, w2d
+        torch.cuda.synchronize()
+        configs = {"quantize_" + cfg.name: q}
+        for name in OTHER_CONFIGS:
+            c = MI.CONFIGS[name]
+            r = run_layer(c, CONFIG_STEPS, CONFIG_WARMUP, args.seed, "auto", "auto", moe, torch,
+                          dev)
+            g2, d2, l2 = rooflines(c, r)
+            configs[name] = {"workload": c.description, "tokens_per_s": c.T / (r["ms_per_step"] * 1e-3),
+                             "ms_per_step": r["ms_per_step"], "steps": CONFIG_STEPS,
+                             "warmup": CONFIG_WARMUP, "stage_ms": r["stage_ms"],
+                             "expert_algorithm": "grouped gemm" if r["gemm"] else "weight streaming",
+                             "roofline": g2, "roofline_down": d2, "layer_roofline": l2}
+            print("config %s: %.1f us/step" % (name, r["ms_per_step"] * 1e3), file=sys.stderr,
+                  flush=True)
+        result["configs"] = configs
+        result["probes"] = probes(torch, dev)
     if not args.no_cpu_baseline:
-        tokens = None
-        if cfg.T > 64:
-            rng = np.random.default_rng(0)
-            tokens = np.sort(rng.choice(cfg.T, size=16, replace=False))
-        result["cpu_baseline"] = cpu_baseline(cfg, (x, wr, b, w13, w2), tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, run["inputs"])
     print(json.dumps(result), flush=True)
     return 0
 

@@ -1,4 +1,5 @@
-"""Build libmoe_mxfp4.so in-tree with hipcc for gfx950.
+"""Build libmoe_mxfp4.so (the layer) and libmoe_probe.so (achievable-peak
+microbenchmarks) in-tree with hipcc for gfx950.
 
     python -m mxfp4_quantized_mixture_amd.build
 """
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
 SOURCES = ["quantize.hip", "route.hip", "expert_mlp.hip", "expert_gemm.hip", "api.hip"]
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -24,10 +27,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libmoe_mxfp4.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _compile(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -38,8 +40,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source: libmoe_mxfp4.so and libmoe_probe.so (always
+    recompiles).  Returns the layer library's path."""
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -50,6 +50,25 @@ def test_no_internal_symbols_exported():
     assert set(text_syms) == set(declared_functions())
 
 
+def test_probe_library_exports_its_header():
+    from mxfp4_quantized_mixture_amd import build as B
+    text = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
+    declared = set(re.findall(r"MOE_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
+    assert declared == {"moe_probe_read", "moe_probe_mfma", "moe_probe_mfma_flops"}
+    out = os.popen("nm -D --defined-only %s" % B.PROBE_LIB).read()
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == declared
+    P = ctypes.CDLL(B.PROBE_LIB)
+    P.moe_probe_mfma_flops.restype = ctypes.c_double
+    assert P.moe_probe_mfma_flops(1) == 2 * 32 * 32 * 64
+    assert P.moe_probe_mfma_flops(4) == 2 * 32 * 32 * 16
+    assert P.moe_probe_mfma_flops(9) == 0
+    P.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    assert P.moe_probe_read(None, 1 << 20, 8, FAKE, None) == 1        # bad arguments
+    assert P.moe_probe_read(FAKE + 4, 1 << 20, 8, FAKE, None) == 1    # misaligned
+    assert P.moe_probe_mfma(9, 8, 1, FAKE, None) == 4                 # unknown kind
+
+
 def test_status_strings(L):
     assert L.moe_status_string(OK) == b"ok"
     names = set()
