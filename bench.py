@@ -23,7 +23,10 @@ taken on the current kernel source, else null.  `cpu_baseline` is the
 single-threaded fp64 CPU oracle on a bounded sample of the same workload.
 With the headline workload (and without --no-configs) the line also carries
 `configs`: the other four workloads and the headline's separately timed
-mxfp4_quantize, each with its own timing and roofline; and `probes`: the
+mxfp4_quantize, each with its own timing and roofline, plus the two decode
+workloads run again with bf16 expert weights (moe_expert_mlp_bf16, the
+comparison path the pages name) with their weight-byte and time ratios to
+the MXFP4 runs; and `probes`: the
 achievable HBM read rate and matrix-core rates measured on this GPU.
 """
 
@@ -50,6 +53,8 @@ NCOPIES = 3
 HEADLINE = "gptoss120b_prefill_skewed"
 OTHER_CONFIGS = ["tiny", "gptoss20b_decode", "gptoss120b_decode", "gptoss20b_prefill"]
 CONFIG_STEPS, CONFIG_WARMUP = 100, 10
+# decode workloads also run with bf16 expert weights (the comparison path)
+BF16_COMPARISON = ["gptoss20b_decode", "gptoss120b_decode"]
 ACT_TERMS = 3                  # grouped GEMM: x and h as 3 fp6 terms
 
 
@@ -183,6 +188,36 @@ def bf16_dev(torch, dev, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
+def time_layers(layers, steps, warmup, moe, torch):
+    """Warm up, then time `steps` steps rotating over the prepared layers
+    (the weight copies): region 1 (the `value` region) with nothing but the
+    layer on the stream, region 2 with HIP events recorded on the layer's
+    stream around each expert kernel.  Returns (total ms of region 1, mean
+    per-stage ms of region 2)."""
+    n = len(layers)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        layers[i % n]()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        layers[i % n]()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evarr = [moe.PreparedLayer.event_array(e) for e in ev]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        layers[i % n](evarr[i])
+    torch.cuda.synchronize()
+    stage = {"gate_up": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+             "down": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+             "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))}
+    return total_ms, stage
+
+
 def run_layer(cfg, steps, warmup, seed, algo, layout, moe, torch, dev, keep_inputs=False):
     """Quantize, time `steps` layer steps (value region, then a second region
     with per-stage events) and return timings plus what the rooflines need."""
@@ -207,29 +242,7 @@ def run_layer(cfg, steps, warmup, seed, algo, layout, moe, torch, dev, keep_inpu
     algo_id = {"auto": moe.MLP_AUTO, "stream": moe.MLP_STREAM, "gemm": moe.MLP_GROUPED_GEMM}[algo]
     layers = [moe.PreparedLayer(xd, wrd, bd, w, cfg.k, out, routing, route_ws, mlp_ws, algo=algo_id)
               for w in copies]
-    torch.cuda.synchronize()
-    for i in range(warmup):
-        layers[i % NCOPIES]()
-    # Timed region 1 (value): the layer alone, nothing else on the stream.
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(steps):
-        layers[i % NCOPIES]()
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    # Timed region 2 (per-kernel durations): the same steps with HIP events
-    # recorded on the layer's stream around each expert kernel.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    evarr = [moe.PreparedLayer.event_array(e) for e in ev]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        layers[i % NCOPIES](evarr[i])
-    torch.cuda.synchronize()
-    stage = {"gate_up": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
-             "down": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
-             "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))}
+    total_ms, stage = time_layers(layers, steps, warmup, moe, torch)
     res = dict(ms_per_step=total_ms / steps, stage_ms=stage, counts=routing.counts.cpu().numpy(),
                packed=packed, gemm=uses_grouped_gemm(cfg, algo))
     if keep_inputs:
@@ -238,6 +251,59 @@ def run_layer(cfg, steps, warmup, seed, algo, layout, moe, torch, dev, keep_inpu
     del layers, copies, base, mlp_ws, route_ws
     torch.cuda.synchronize()
     return res
+
+
+def run_layer_bf16(cfg, steps, warmup, seed, moe, torch, dev):
+    """The same layer with bf16 expert weights (moe_expert_mlp_bf16, the
+    comparison path): same inputs, routing and timing protocol as run_layer,
+    NCOPIES weight copies rotated.  Returns timings and HBM rooflines of its
+    two expert kernels, priced with the bf16 weight bytes."""
+    from synth import moe_inputs as MI
+
+    wr, b = MI.gen_router(cfg, seed)
+    x = MI.gen_x(cfg, seed)
+    w13, w2 = MI.gen_experts(cfg, seed, threads=16)
+    xd, wrd, bd = bf16_dev(torch, dev, x), torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)
+    base = (bf16_dev(torch, dev, w13), bf16_dev(torch, dev, w2))
+    del w13, w2
+    copies = [base] + [(base[0].clone(), base[1].clone()) for _ in range(NCOPIES - 1)]
+    out = torch.empty(cfg.T, cfg.D, dtype=torch.bfloat16, device=dev)
+    routing = moe.alloc_routing(cfg.T, cfg.E, cfg.k, dev)
+    route_ws = moe.route_workspace(cfg.T, cfg.D, cfg.E, cfg.k, dev)
+    mlp_ws = moe.mlp_bf16_workspace(cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, dev)
+    layers = [moe.PreparedLayer(xd, wrd, bd, w, cfg.k, out, routing, route_ws, mlp_ws)
+              for w in copies]
+    total_ms, st = time_layers(layers, steps, warmup, moe, torch)
+    counts = routing.counts.cpu().numpy()
+    del layers, copies, base, mlp_ws, route_ws
+    torch.cuda.synchronize()
+    touched = int((counts > 0).sum())
+    D, F = cfg.D, cfg.F
+    gu_bytes = touched * 2 * F * D * 2 + 2 * cfg.T * D
+    dn_bytes = touched * D * F * 2
+
+    def hbm(bytes_, ms, kernel):
+        a = bytes_ / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS, "kernel": kernel, "algorithmic_per_launch": bytes_,
+                "avg_launch_ms": ms}
+
+    ms = total_ms / steps
+    return {"workload": cfg.description + ", bf16 expert weights", "expert_weights": "bf16",
+            "tokens_per_s": cfg.T / (ms * 1e-3), "ms_per_step": ms, "steps": steps,
+            "warmup": warmup, "stage_ms": st, "touched_experts": touched,
+            "roofline": hbm(gu_bytes, st["gate_up"], "expert_bf16_kernel<gate_up>"),
+            "roofline_down": hbm(dn_bytes, st["down"], "expert_bf16_kernel<down>")}
+
+
+def bf16_comparison(cfg, mx, bf) -> dict:
+    """Weight bytes and times of the bf16 path relative to the MXFP4 one."""
+    w_mx = mx["roofline"]["algorithmic_per_launch"] - 2 * cfg.T * cfg.D
+    w_bf = bf["roofline"]["algorithmic_per_launch"] - 2 * cfg.T * cfg.D
+    return {"gate_up_weight_bytes_ratio": w_bf / w_mx,
+            "gate_up_time_ratio": bf["stage_ms"]["gate_up"] / mx["stage_ms"]["gate_up"],
+            "down_time_ratio": bf["stage_ms"]["down"] / mx["stage_ms"]["down"],
+            "step_time_ratio": bf["ms_per_step"] / mx["ms_per_step"]}
 
 
 def rooflines(cfg, run) -> tuple[dict, dict, dict]:
@@ -379,6 +445,9 @@ def main() -> int:
                          "workload's expert weights (W13 and W2)")
     ap.add_argument("--probes", action="store_true",
                     help="only run the achievable-peak probes (HBM read, matrix cores)")
+    ap.add_argument("--bf16-weights", action="store_true",
+                    help="only run the bf16-weight comparison path (moe_expert_mlp_bf16) on the "
+                         "workload")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a kernel of known traffic)")
@@ -414,6 +483,14 @@ def main() -> int:
         print(json.dumps({"metric": "mxfp4_quantize HBM GB/s",
                           "workload": "%s: all %d experts' W13 and W2" % (cfg.name, cfg.E),
                           "results": q}), flush=True)
+        return 0
+
+    if args.bf16_weights:
+        r = run_layer_bf16(cfg, args.steps, args.warmup, args.seed, moe, torch, dev)
+        print(json.dumps({"metric": "MXFP4 MoE-layer tokens/s, bf16-weight comparison path",
+                          "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "config": {"workload": cfg.description, "name": cfg.name},
+                          "bf16_weights": r}), flush=True)
         return 0
 
     headline = args.workload == HEADLINE and not args.no_configs
@@ -471,6 +548,12 @@ def main() -> int:
                              "roofline": g2, "roofline_down": d2, "layer_roofline": l2}
             print("config %s: %.1f us/step" % (name, r["ms_per_step"] * 1e3), file=sys.stderr,
                   flush=True)
+            if name in BF16_COMPARISON:
+                bf = run_layer_bf16(c, CONFIG_STEPS, CONFIG_WARMUP, args.seed, moe, torch, dev)
+                bf["vs_mxfp4"] = bf16_comparison(c, configs[name], bf)
+                configs["bf16_weights_" + name] = bf
+                print("config %s, bf16 weights: %.1f us/step" % (name, bf["ms_per_step"] * 1e3),
+                      file=sys.stderr, flush=True)
         result["configs"] = configs
         result["probes"] = probes(torch, dev)
     if not args.no_cpu_baseline:

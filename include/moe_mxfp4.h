@@ -54,7 +54,7 @@
 /* Version of this ABI; moe_abi_version() returns it.  Bumped on any
  * incompatible change (2: status codes and argument order of the contract,
  * stage events only in moe_expert_mlp_ex). */
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Size of the fixed device workspace of moe_expert_mlp_noalloc (16 MiB). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
@@ -293,6 +293,52 @@ MOE_API moe_status_t moe_expert_mlp_ex(const uint16_t *x, const uint8_t *w13_q,
                                        int32_t F, int32_t E, int32_t k, uint16_t *out,
                                        void *ws, size_t ws_bytes, int algo,
                                        hipEvent_t *stage_events, hipStream_t stream);
+
+/*
+ * moe_expert_mlp_bf16 -- the same layer (steps and combine as moe_expert_mlp)
+ * on bf16 expert weights: the fallback the pages name for hardware without
+ * MXFP4 kernels, at about four times the weight bytes ("Tricks" section 7;
+ * Japanese Transformers page, "メモリ削減効果").  A comparison path: it lets
+ * both weight formats run on the same layer and be measured side by side.
+ *   x        [T, D] bf16 bits (read only)
+ *   w13      [E, 2F, D] bf16 bits (read only): rows 0..F-1 gate, F..2F-1 up
+ *   w2       [E, D, F] bf16 bits (read only)
+ *   topk_w, offsets, sorted_pairs, pair_pos: as written by moe_route
+ *   out      [T, D] bf16 bits (written)
+ *   ws, ws_bytes workspace of at least moe_expert_mlp_bf16_workspace_size(T,
+ *            D, F, E, k) bytes (scratch)
+ * Arithmetic: weight streaming on bf16 matrix-core products (each expert's
+ * weights are read once per group of 16 of its pairs: meant for decode-sized
+ * batches); x and the weights enter exactly, products are exact and
+ * accumulate in fp32; h is kept in fp32 and enters the down products as two
+ * bf16 terms (error below 2^-17 of |h|); y and the combine in fp32; output
+ * rounded to bf16 (nearest even).
+ * Preconditions: as moe_route, plus 32 <= F, F % 32 == 0, the routing arrays
+ * consistent with each other; x, w13, w2, out and ws 16-byte aligned.
+ * Errors: MOE_ERR_SHAPE, MOE_ERR_NULL, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN,
+ * MOE_ERR_DEVICE, MOE_ERR_HIP.  moe_expert_mlp_bf16_workspace_size returns 0
+ * for shapes the call rejects.
+ *
+ * moe_expert_mlp_bf16_ex -- the same with optional instrumentation:
+ * stage_events is NULL or 4 events, recorded as for moe_expert_mlp_ex.
+ */
+MOE_API size_t moe_expert_mlp_bf16_workspace_size(int32_t T, int32_t D, int32_t F,
+                                                  int32_t E, int32_t k);
+MOE_API moe_status_t moe_expert_mlp_bf16(const uint16_t *x, const uint16_t *w13,
+                                         const uint16_t *w2, const float *topk_w,
+                                         const int32_t *offsets,
+                                         const int32_t *sorted_pairs,
+                                         const int32_t *pair_pos, int32_t T, int32_t D,
+                                         int32_t F, int32_t E, int32_t k, uint16_t *out,
+                                         void *ws, size_t ws_bytes, hipStream_t stream);
+MOE_API moe_status_t moe_expert_mlp_bf16_ex(const uint16_t *x, const uint16_t *w13,
+                                            const uint16_t *w2, const float *topk_w,
+                                            const int32_t *offsets,
+                                            const int32_t *sorted_pairs,
+                                            const int32_t *pair_pos, int32_t T, int32_t D,
+                                            int32_t F, int32_t E, int32_t k, uint16_t *out,
+                                            void *ws, size_t ws_bytes,
+                                            hipEvent_t *stage_events, hipStream_t stream);
 
 /*
  * moe_expert_mlp_noalloc -- moe_expert_mlp_ex without a workspace argument

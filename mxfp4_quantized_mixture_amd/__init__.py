@@ -34,7 +34,7 @@ __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "mxfp4_pack", "moe_route", "moe
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 NOALLOC_SCRATCH_BYTES = 16 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 SCALE_FLOOR_DIV6 = 0
 SCALE_OCP = 1
@@ -95,6 +95,14 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_mlp_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                              P, ctypes.c_int, P]
         L.moe_expert_mlp_noalloc.restype = ctypes.c_int
+        L.moe_expert_mlp_bf16_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_expert_mlp_bf16_workspace_size.restype = sz
+        L.moe_expert_mlp_bf16.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                          P, P, sz, P]
+        L.moe_expert_mlp_bf16.restype = ctypes.c_int
+        L.moe_expert_mlp_bf16_ex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                             P, P, sz, P, P]
+        L.moe_expert_mlp_bf16_ex.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -311,6 +319,37 @@ def moe_expert_mlp_noalloc(x: torch.Tensor, weights: ExpertWeights, routing: Rou
     return out
 
 
+def mlp_bf16_workspace(T: int, D: int, F: int, E: int, k: int, device) -> torch.Tensor:
+    n = lib().moe_expert_mlp_bf16_workspace_size(T, D, F, E, k)
+    if n == 0:
+        raise MoEError("moe_expert_mlp_bf16_workspace_size", 2)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_expert_mlp_bf16(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, routing: Routing,
+                        out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                        events=None) -> torch.Tensor:
+    """The expert layer on bf16 weights: w13 [E, 2F, D], w2 [E, D, F] (the
+    comparison path of the MXFP4 one; same routing and output)."""
+    T, D = x.shape
+    E, F2, D13 = w13.shape
+    F = F2 // 2
+    k = routing.ids.shape[1]
+    if D13 != D or F2 != 2 * F or tuple(w2.shape) != (E, D, F):
+        raise ValueError("bf16 expert weights must be [E, 2F, D] and [E, D, F]")
+    out = out if out is not None else torch.empty(T, D, dtype=torch.bfloat16, device=x.device)
+    ws = ws if ws is not None else mlp_bf16_workspace(T, D, F, E, k, x.device)
+    ev = None if events is None else _event_array(events)
+    _check("moe_expert_mlp_bf16", lib().moe_expert_mlp_bf16_ex(
+        _dev(x, "x", torch.bfloat16), _dev(w13, "w13", torch.bfloat16),
+        _dev(w2, "w2", torch.bfloat16), _dev(routing.weights, "topk_w", torch.float32),
+        _dev(routing.offsets, "offsets", torch.int32),
+        _dev(routing.sorted_pairs, "sorted_pairs", torch.int32),
+        _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
+        _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), ev, _stream(x.device)))
+    return out
+
+
 class MoELayer:
     """Router + MXFP4 experts with preallocated routing buffers and workspaces."""
 
@@ -341,14 +380,23 @@ class PreparedLayer:
     """
 
     def __init__(self, x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None,
-                 weights: ExpertWeights, k: int, out: torch.Tensor, routing: Routing,
+                 weights, k: int, out: torch.Tensor, routing: Routing,
                  route_ws: torch.Tensor, mlp_ws: torch.Tensor, stream=None,
                  algo: int = MLP_AUTO):
+        """weights: ExpertWeights (MXFP4, moe_expert_mlp_ex), or a (w13, w2)
+        pair of bf16 tensors [E, 2F, D], [E, D, F] (moe_expert_mlp_bf16_ex)."""
         T, D = x.shape
-        E, F = weights.E, weights.F
         self.L = lib()
         st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
         self._keep = (x, wr, br, weights, out, routing, route_ws, mlp_ws)
+        self.bf16 = not isinstance(weights, ExpertWeights)
+        if self.bf16:
+            w13, w2 = weights
+            E, F = w13.shape[0], w13.shape[1] // 2
+            if tuple(w13.shape) != (E, 2 * F, D) or tuple(w2.shape) != (E, D, F):
+                raise ValueError("bf16 expert weights must be [E, 2F, D] and [E, D, F]")
+        else:
+            E, F = weights.E, weights.F
         self.route_args = (
             _dev(x, "x", torch.bfloat16), _dev(wr, "wr", torch.float32),
             None if br is None else _dev(br, "br", torch.float32), T, D, E, k,
@@ -356,13 +404,18 @@ class PreparedLayer:
             _dev(routing.counts, "counts"), _dev(routing.offsets, "offsets"),
             _dev(routing.sorted_pairs, "sorted_pairs"), _dev(routing.pair_pos, "pair_pos"),
             None, _dev(route_ws, "ws"), route_ws.numel(), st)
-        self.mlp_head = (
-            _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
-            _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
-            _dev(weights.w2_s, "w2_s", torch.uint8), _dev(routing.weights, "topk_w"),
-            _dev(routing.offsets, "offsets"), _dev(routing.sorted_pairs, "sorted_pairs"),
-            _dev(routing.pair_pos, "pair_pos"), T, D, F, E, k, _dev(out, "out", torch.bfloat16),
-            _dev(mlp_ws, "ws"), mlp_ws.numel(), algo | weights.algo_flags)
+        tail = (_dev(routing.weights, "topk_w"), _dev(routing.offsets, "offsets"),
+                _dev(routing.sorted_pairs, "sorted_pairs"), _dev(routing.pair_pos, "pair_pos"),
+                T, D, F, E, k, _dev(out, "out", torch.bfloat16), _dev(mlp_ws, "ws"),
+                mlp_ws.numel())
+        if self.bf16:
+            self.mlp_head = (_dev(x, "x", torch.bfloat16), _dev(w13, "w13", torch.bfloat16),
+                             _dev(w2, "w2", torch.bfloat16)) + tail
+        else:
+            self.mlp_head = (
+                _dev(x, "x", torch.bfloat16), _dev(weights.w13_q, "w13_q", torch.uint8),
+                _dev(weights.w13_s, "w13_s", torch.uint8), _dev(weights.w2_q, "w2_q", torch.uint8),
+                _dev(weights.w2_s, "w2_s", torch.uint8)) + tail + (algo | weights.algo_flags,)
         self.stream = st
 
     @staticmethod
@@ -373,6 +426,9 @@ class PreparedLayer:
         s = self.L.moe_route(*self.route_args)
         if s:
             raise MoEError("moe_route", s)
-        s = self.L.moe_expert_mlp_ex(*self.mlp_head, event_array, self.stream)
+        if self.bf16:
+            s = self.L.moe_expert_mlp_bf16_ex(*self.mlp_head, event_array, self.stream)
+        else:
+            s = self.L.moe_expert_mlp_ex(*self.mlp_head, event_array, self.stream)
         if s:
-            raise MoEError("moe_expert_mlp", s)
+            raise MoEError("moe_expert_mlp_bf16" if self.bf16 else "moe_expert_mlp", s)

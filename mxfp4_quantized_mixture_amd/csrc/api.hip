@@ -207,6 +207,39 @@ moe_status_t moe_expert_mlp_ex(const uint16_t* x, const uint8_t* w13_q, const ui
                                       stream));
 }
 
+size_t moe_expert_mlp_bf16_workspace_size(int32_t T, int32_t D, int32_t F, int32_t E,
+                                          int32_t k) {
+    if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return 0;
+    return moe::bf16_mlp_workspace_bytes(T, D, F, k);
+}
+
+moe_status_t moe_expert_mlp_bf16_ex(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                                    const float* topk_w, const int32_t* offsets,
+                                    const int32_t* sorted_pairs, const int32_t* pair_pos,
+                                    int32_t T, int32_t D, int32_t F, int32_t E, int32_t k,
+                                    uint16_t* out, void* ws, size_t ws_bytes,
+                                    hipEvent_t* stage_events, hipStream_t stream) {
+    if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return MOE_ERR_SHAPE;
+    if (!x || !w13 || !w2 || !topk_w || !offsets || !sorted_pairs || !pair_pos || !out)
+        return MOE_ERR_NULL;
+    if (!ws || ws_bytes < moe::bf16_mlp_workspace_bytes(T, D, F, k)) return MOE_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
+    return hip_status(moe::launch_mlp_bf16(T, D, F, E, k, x, w13, w2, topk_w, offsets,
+                                           sorted_pairs, pair_pos, out, ws, stage_events,
+                                           stream));
+}
+
+moe_status_t moe_expert_mlp_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                                 const float* topk_w, const int32_t* offsets,
+                                 const int32_t* sorted_pairs, const int32_t* pair_pos, int32_t T,
+                                 int32_t D, int32_t F, int32_t E, int32_t k, uint16_t* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+    return moe_expert_mlp_bf16_ex(x, w13, w2, topk_w, offsets, sorted_pairs, pair_pos, T, D, F,
+                                  E, k, out, ws, ws_bytes, nullptr, stream);
+}
+
 moe_status_t moe_expert_mlp_noalloc(const uint16_t* x, const uint8_t* w13_q,
                                     const uint8_t* w13_s, const uint8_t* w2_q,
                                     const uint8_t* w2_s, const float* topk_w,

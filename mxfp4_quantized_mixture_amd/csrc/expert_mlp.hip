@@ -608,15 +608,21 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
 static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
                                  const int32_t* pos, uint16_t* out, hipEvent_t* events,
                                  hipStream_t stream) {
+    return launch_combine_rows(p.T, p.D, p.k, y, topk_w, pos, out, events, stream);
+}
+
+hipError_t launch_combine_rows(int T, int D, int k, const float* y, const float* topk_w,
+                               const int32_t* pos, uint16_t* out, hipEvent_t* events,
+                               hipStream_t stream) {
     if (events) {
         const hipError_t er = hipEventRecord(events[2], stream);
         if (er != hipSuccess) return er;
     }
-    const int64_t n = (int64_t)p.T * (p.D / 4);
+    const int64_t n = (int64_t)T * (D / 4);
     int64_t gb = (n + 255) / 256;
     if (gb > 8192) gb = 8192;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)gb), dim3(256), 0, stream, y, topk_w, pos,
-                       p.T, p.D, p.k, out);
+                       T, D, k, out);
     if (events) {
         const hipError_t er = hipEventRecord(events[3], stream);
         if (er != hipSuccess) return er;

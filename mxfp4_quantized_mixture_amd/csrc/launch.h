@@ -64,4 +64,18 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
                            const int32_t* offsets, const int32_t* sorted, float* y, char* base,
                            hipEvent_t* events, hipStream_t stream);
 
+// out[t] = bf16(sum_j topk_w[t, j] y[pos[t k + j]]), slots in order
+// (expert_mlp.hip); events, if given, are recorded as stage events 2 and 3
+hipError_t launch_combine_rows(int T, int D, int k, const float* y, const float* topk_w,
+                               const int32_t* pos, uint16_t* out, hipEvent_t* events,
+                               hipStream_t stream);
+
+// bf16-weight comparison path (expert_bf16.hip): workspace = y fp32 [P, D]
+// then h fp32 [P, F]
+size_t bf16_mlp_workspace_bytes(int T, int D, int F, int k);
+hipError_t launch_mlp_bf16(int T, int D, int F, int E, int k, const uint16_t* x,
+                           const uint16_t* w13, const uint16_t* w2, const float* topk_w,
+                           const int32_t* offsets, const int32_t* sorted, const int32_t* pos,
+                           uint16_t* out, void* ws, hipEvent_t* events, hipStream_t stream);
+
 }  // namespace moe

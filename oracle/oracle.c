@@ -387,31 +387,21 @@ int oracle_route(const uint16_t *x, const float *wr, const float *b,
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* One expert applied to a list of tokens:
+/* One expert on widened (fp64) weights, applied to a list of tokens:
  *   y[i, :] = W2 h,  h = silu(Wg x_t) * (Wu x_t),  t = toks[i], i < n.
  *   x    bf16 [T, D] (only the listed rows are read)
- *   q13  [2F, D/2], s13 [2F, D/32]: gate rows 0..F-1, up rows F..2F-1
- *   q2   [D, F/2],  s2  [D, F/32]
+ *   w13  fp64 [2F, D]: gate rows 0..F-1, up rows F..2F-1;  w2 fp64 [D, F]
  *   y    fp64 [n, D]
- * SwiGLU experts: [WELCOME] s.4; weights kept in MXFP4 and widened only for
- * the arithmetic: [TALK] hardware section, [TRICKS] s.8.  The expert's
- * weights are widened to fp64 once, then each token is a plain loop. */
-int oracle_expert_mlp(const uint16_t *x, int D, int F, const uint8_t *q13,
-                      const uint8_t *s13, const uint8_t *q2, const uint8_t *s2,
-                      const int32_t *toks, int n, double *y)
+ * SwiGLU experts: [WELCOME] s.4.  Each token is a plain loop. */
+static int expert_mlp_dense(const uint16_t *x, int D, int F, const double *w13,
+                            const double *w2, const int32_t *toks, int n, double *y)
 {
-    if (D % 32 != 0 || F % 32 != 0)
-        return -1;
-    double *w13 = (double *)malloc(sizeof(double) * (size_t)2 * F * D);
-    double *w2 = (double *)malloc(sizeof(double) * (size_t)D * F);
     double *xd = (double *)malloc(sizeof(double) * (size_t)D);
     double *h = (double *)malloc(sizeof(double) * (size_t)F);
-    if (!w13 || !w2 || !xd || !h) {
-        free(w13); free(w2); free(xd); free(h);
+    if (!xd || !h) {
+        free(xd); free(h);
         return -2;
     }
-    oracle_dequantize(q13, s13, 2 * F, D, w13);
-    oracle_dequantize(q2, s2, D, F, w2);
     for (int i = 0; i < n; ++i) {
         int t = toks[i];
         for (int d = 0; d < D; ++d)
@@ -431,8 +421,56 @@ int oracle_expert_mlp(const uint16_t *x, int D, int F, const uint8_t *q13,
             y[(int64_t)i * D + d] = acc;
         }
     }
-    free(w13); free(w2); free(xd); free(h);
+    free(xd); free(h);
     return 0;
+}
+
+/* One expert on MXFP4 weights:
+ *   q13  [2F, D/2], s13 [2F, D/32]: gate rows 0..F-1, up rows F..2F-1
+ *   q2   [D, F/2],  s2  [D, F/32]
+ * other arguments as expert_mlp_dense.  The weights stay in MXFP4 and are
+ * widened only for the arithmetic ([TALK] hardware section, [TRICKS] s.8):
+ * here once per call, to fp64. */
+int oracle_expert_mlp(const uint16_t *x, int D, int F, const uint8_t *q13,
+                      const uint8_t *s13, const uint8_t *q2, const uint8_t *s2,
+                      const int32_t *toks, int n, double *y)
+{
+    if (D % 32 != 0 || F % 32 != 0)
+        return -1;
+    double *w13 = (double *)malloc(sizeof(double) * (size_t)2 * F * D);
+    double *w2 = (double *)malloc(sizeof(double) * (size_t)D * F);
+    if (!w13 || !w2) {
+        free(w13); free(w2);
+        return -2;
+    }
+    oracle_dequantize(q13, s13, 2 * F, D, w13);
+    oracle_dequantize(q2, s2, D, F, w2);
+    int rc = expert_mlp_dense(x, D, F, w13, w2, toks, n, y);
+    free(w13); free(w2);
+    return rc;
+}
+
+/* One expert on bf16 weights (the bf16 fallback the pages compare MXFP4 with,
+ * [TRICKS] s.7): w13 bf16 [2F, D], w2 bf16 [D, F], widened to fp64 exactly;
+ * other arguments as expert_mlp_dense. */
+int oracle_expert_mlp_bf16(const uint16_t *x, int D, int F, const uint16_t *w13b,
+                           const uint16_t *w2b, const int32_t *toks, int n, double *y)
+{
+    if (D < 1 || F < 1)
+        return -1;
+    double *w13 = (double *)malloc(sizeof(double) * (size_t)2 * F * D);
+    double *w2 = (double *)malloc(sizeof(double) * (size_t)D * F);
+    if (!w13 || !w2) {
+        free(w13); free(w2);
+        return -2;
+    }
+    for (int64_t i = 0; i < (int64_t)2 * F * D; ++i)
+        w13[i] = oracle_bf16_to_double(w13b[i]);
+    for (int64_t i = 0; i < (int64_t)D * F; ++i)
+        w2[i] = oracle_bf16_to_double(w2b[i]);
+    int rc = expert_mlp_dense(x, D, F, w13, w2, toks, n, y);
+    free(w13); free(w2);
+    return rc;
 }
 
 /* The whole layer for the tokens listed in toks[0..ntok) (all T tokens in

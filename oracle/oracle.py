@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_moe.restype = i32
         L.oracle_expert_mlp.argtypes = [P, i32, i32, P, P, P, P, P, i32, P]
         L.oracle_expert_mlp.restype = i32
+        L.oracle_expert_mlp_bf16.argtypes = [P, i32, i32, P, P, P, i32, P]
+        L.oracle_expert_mlp_bf16.restype = i32
         _lib = L
     return _lib
 
@@ -193,13 +195,32 @@ def expert_mlp(x_bf16, q13e, s13e, q2e, s2e, F: int, tokens) -> np.ndarray:
     return y
 
 
+def expert_mlp_bf16(x_bf16, w13e, w2e, F: int, tokens) -> np.ndarray:
+    """One expert with bf16 weights (w13e [2F, D], w2e [D, F] as bf16 bit
+    patterns) on the listed tokens: y [n, D] fp64 (see oracle_expert_mlp_bf16)."""
+    x = _c(x_bf16, np.uint16)
+    D = x.shape[1]
+    w13e, w2e = _c(w13e, np.uint16), _c(w2e, np.uint16)
+    if w13e.shape != (2 * F, D) or w2e.shape != (D, F):
+        raise ValueError("bf16 expert weights must be [2F, D] and [D, F]")
+    toks = _c(tokens, np.int32)
+    y = np.empty((len(toks), D), np.float64)
+    rc = lib().oracle_expert_mlp_bf16(_ptr(x), D, F, _ptr(w13e), _ptr(w2e), _ptr(toks),
+                                      len(toks), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_expert_mlp_bf16 failed (rc=%d)" % rc)
+    return y
+
+
 def moe_threaded(x_bf16, expert_weights, ids, w, F: int, tokens=None, threads: int = 8):
     """Same result as moe(), with experts evaluated on parallel threads.
 
-    expert_weights(e) -> (q13e, s13e, q2e, s2e) returns expert e's MXFP4
-    arrays (so experts can be quantized lazily, on the worker threads).  Each
-    worker runs the single-threaded oracle_expert_mlp; the slot-order combine
-    out[t] = sum_j w[t, j] * y(t, j) is then done here in fp64, j ascending.
+    expert_weights(e) returns expert e's weights (so experts can be prepared
+    lazily, on the worker threads): either its MXFP4 arrays (q13e, s13e, q2e,
+    s2e), evaluated by oracle_expert_mlp, or its bf16 matrices (w13e, w2e),
+    evaluated by oracle_expert_mlp_bf16.  Each worker runs the single-threaded
+    oracle; the slot-order combine out[t] = sum_j w[t, j] * y(t, j) is then
+    done here in fp64, j ascending.
     """
     ids = np.asarray(ids)
     T, k = ids.shape
@@ -212,9 +233,13 @@ def moe_threaded(x_bf16, expert_weights, ids, w, F: int, tokens=None, threads: i
             jobs.setdefault(int(ids[t, j]), []).append((i, j, int(t)))
 
     def run(e):
-        q13e, s13e, q2e, s2e = expert_weights(e)
+        we = expert_weights(e)
         lst = jobs[e]
-        ye = expert_mlp(x_bf16, q13e, s13e, q2e, s2e, F, [t for _, _, t in lst])
+        tl = [t for _, _, t in lst]
+        if len(we) == 2:
+            ye = expert_mlp_bf16(x_bf16, we[0], we[1], F, tl)
+        else:
+            ye = expert_mlp(x_bf16, *we, F, tl)
         for r, (i, j, _) in enumerate(lst):
             y[i, j] = ye[r]
 

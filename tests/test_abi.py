@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     assert {"mxfp4_quantize", "mxfp4_quantize_ex", "mxfp4_pack", "moe_route", "moe_expert_mlp",
             "moe_route_workspace_size",
             "moe_expert_mlp_workspace_size", "moe_status_string", "mxfp4_dequantize",
-            "moe_abi_version"} <= names
+            "moe_abi_version", "moe_expert_mlp_bf16", "moe_expert_mlp_bf16_ex",
+            "moe_expert_mlp_bf16_workspace_size"} <= names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -78,7 +79,7 @@ def test_status_strings(L):
     assert len(names) == 7
     assert b"gfx950" in L.moe_status_string(DEVICE)
     assert L.moe_status_string(99) == b"unknown status"
-    assert L.moe_abi_version() == 2 == moe.ABI_VERSION
+    assert L.moe_abi_version() == 3 == moe.ABI_VERSION
 
 
 def test_header_status_codes_match():
@@ -206,6 +207,29 @@ def test_mlp_workspace_covers_both_algorithms(L):
     assert n >= y + P * (F // 64) * 160 + T * (D // 64) * 160
 
 
+def _bf16(L, T=8, D=64, F=64, E=4, k=2, out=FAKE, ws_bytes=None, w13=FAKE, events=None):
+    if ws_bytes is None:
+        ws_bytes = L.moe_expert_mlp_bf16_workspace_size(T, D, F, E, k) or 1 << 20
+    return L.moe_expert_mlp_bf16_ex(FAKE, w13, FAKE, FAKE, FAKE, FAKE, FAKE, T, D, F, E, k, out,
+                                    FAKE, ws_bytes, events, None)
+
+
+def test_bf16_mlp_workspace_and_validation(L):
+    T, D, F, E, k = 32, 2880, 2880, 32, 4
+    assert L.moe_expert_mlp_bf16_workspace_size(T, D, F, E, k) >= 4 * T * k * (D + F)
+    assert L.moe_expert_mlp_bf16_workspace_size(8, 64, 48, 4, 2) == 0   # F % 32
+    assert L.moe_expert_mlp_bf16_workspace_size(0, 64, 64, 4, 2) == 0   # T < 1
+    assert _bf16(L, F=40) == SHAPE
+    assert _bf16(L, D=48) == SHAPE
+    assert _bf16(L, k=5, E=4) == SHAPE
+    assert _bf16(L, out=None) == NULL
+    assert _bf16(L, w13=None) == NULL
+    assert _bf16(L, ws_bytes=100) == WS
+    assert _bf16(L, w13=FAKE + 4) == ALIGN
+    assert L.moe_expert_mlp_bf16(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 64, 40, 4, 2,
+                                 FAKE, FAKE, 1 << 20, None) == SHAPE
+
+
 def _gpu_present():
     import torch
     return torch.cuda.is_available()
@@ -224,8 +248,10 @@ def test_valid_calls_without_a_gfx950_return_device_error(L):
     assert _mlp(L) == DEVICE
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM) == DEVICE
     assert _mlp_ex(L, moe.MLP_AUTO, D=3904) == DEVICE           # taken by the grouped GEMM
+    assert _bf16(L) == DEVICE
     # argument errors still win over the device check
     assert _mlp(L, F=40) == SHAPE
+    assert _bf16(L, F=40) == SHAPE
 
 
 def test_binding_refuses_cpu_tensors():
