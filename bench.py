@@ -26,7 +26,8 @@ With the headline workload (and without --no-configs) the line also carries
 mxfp4_quantize, each with its own timing and roofline, plus the two decode
 workloads run again with bf16 expert weights (moe_expert_mlp_bf16, the
 comparison path the pages name) with their weight-byte and time ratios to
-the MXFP4 runs; and `probes`: the
+the MXFP4 runs, and through moe_layer_decode (routing fused into the gate/up
+weight stream) as `fused_decode`; and `probes`: the
 achievable HBM read rate and matrix-core rates measured on this GPU.
 """
 
@@ -54,7 +55,9 @@ HEADLINE = "gptoss120b_prefill_skewed"
 OTHER_CONFIGS = ["tiny", "gptoss20b_decode", "gptoss120b_decode", "gptoss20b_prefill"]
 CONFIG_STEPS, CONFIG_WARMUP = 100, 10
 # decode workloads also run with bf16 expert weights (the comparison path)
+# and through the fused decode entry point
 BF16_COMPARISON = ["gptoss20b_decode", "gptoss120b_decode"]
+FUSED_DECODE = ["gptoss20b_decode", "gptoss120b_decode"]
 ACT_TERMS = 3                  # grouped GEMM: x and h as 3 fp6 terms
 
 
@@ -294,6 +297,38 @@ def run_layer_bf16(cfg, steps, warmup, seed, moe, torch, dev):
             "warmup": warmup, "stage_ms": st, "touched_experts": touched,
             "roofline": hbm(gu_bytes, st["gate_up"], "expert_bf16_kernel<gate_up>"),
             "roofline_down": hbm(dn_bytes, st["down"], "expert_bf16_kernel<down>")}
+
+
+def run_layer_fused_decode(cfg, steps, warmup, seed, moe, torch, dev):
+    """The same decode step through moe_layer_decode (routing fused into the
+    gate/up weight stream; packed codes): same inputs and timing protocol as
+    run_layer, NCOPIES weight copies rotated."""
+    from synth import moe_inputs as MI
+
+    wr, b = MI.gen_router(cfg, seed)
+    x = MI.gen_x(cfg, seed)
+    w13, w2 = MI.gen_experts(cfg, seed, threads=16)
+    xd, wrd, bd = bf16_dev(torch, dev, x), torch.from_numpy(wr).to(dev), torch.from_numpy(b).to(dev)
+    base = moe.ExpertWeights.quantize(bf16_dev(torch, dev, w13), bf16_dev(torch, dev, w2),
+                                      packed=True)
+    del w13, w2
+    copies = [base] + [moe.ExpertWeights(base.w13_q.clone(), base.w13_s.clone(),
+                                         base.w2_q.clone(), base.w2_s.clone(), True)
+                       for _ in range(NCOPIES - 1)]
+    out = torch.empty(cfg.T, cfg.D, dtype=torch.bfloat16, device=dev)
+    routing = moe.alloc_routing(cfg.T, cfg.E, cfg.k, dev)
+    ws = moe.decode_workspace(cfg.T, cfg.D, cfg.F, cfg.E, cfg.k, dev)
+    layers = [moe.PreparedDecodeLayer(xd, wrd, bd, w, cfg.k, out, routing, ws) for w in copies]
+    total_ms, st = time_layers(layers, steps, warmup, moe, torch)
+    err = moe.decode_error(ws)
+    del layers, copies, base, ws
+    torch.cuda.synchronize()
+    ms = total_ms / steps
+    return {"entry_point": "moe_layer_decode", "tokens_per_s": cfg.T / (ms * 1e-3),
+            "ms_per_step": ms, "steps": steps, "warmup": warmup,
+            "stage_ms": {"route_and_gate_up": st["gate_up"], "down": st["down"],
+                         "combine": st["combine"]},
+            "device_wait_errors": err}
 
 
 def bf16_comparison(cfg, mx, bf) -> dict:
@@ -548,6 +583,14 @@ def main() -> int:
                              "roofline": g2, "roofline_down": d2, "layer_roofline": l2}
             print("config %s: %.1f us/step" % (name, r["ms_per_step"] * 1e3), file=sys.stderr,
                   flush=True)
+            if name in FUSED_DECODE:
+                fd = run_layer_fused_decode(c, CONFIG_STEPS, CONFIG_WARMUP, args.seed, moe, torch,
+                                            dev)
+                fd["step_time_ratio_to_separate_launches"] = (fd["ms_per_step"] /
+                                                             r["ms_per_step"])
+                configs[name]["fused_decode"] = fd
+                print("config %s, fused decode: %.1f us/step" % (name, fd["ms_per_step"] * 1e3),
+                      file=sys.stderr, flush=True)
             if name in BF16_COMPARISON:
                 bf = run_layer_bf16(c, CONFIG_STEPS, CONFIG_WARMUP, args.seed, moe, torch, dev)
                 bf["vs_mxfp4"] = bf16_comparison(c, configs[name], bf)

@@ -54,7 +54,7 @@
 /* Version of this ABI; moe_abi_version() returns it.  Bumped on any
  * incompatible change (2: status codes and argument order of the contract,
  * stage events only in moe_expert_mlp_ex). */
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Size of the fixed device workspace of moe_expert_mlp_noalloc (16 MiB). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
@@ -339,6 +339,69 @@ MOE_API moe_status_t moe_expert_mlp_bf16_ex(const uint16_t *x, const uint16_t *w
                                             int32_t F, int32_t E, int32_t k, uint16_t *out,
                                             void *ws, size_t ws_bytes,
                                             hipEvent_t *stage_events, hipStream_t stream);
+
+/*
+ * moe_layer_decode -- the whole layer for a decode-sized batch (moe_route
+ * followed by moe_expert_mlp with weight streaming) with the routing fused
+ * into the gate/up weight stream: one launch computes the router logits,
+ * the top-k routing and the gate/up experts, its expert blocks issuing
+ * their first weight loads before the routing is known and waiting for it
+ * on the device; the down experts and the combine follow as two more
+ * kernels.  Same layer and arithmetic as moe_route + moe_expert_mlp_ex
+ * (MOE_MLP_STREAM): every output, the routing arrays included, is
+ * bit-identical to theirs ("Welcome GPT OSS" section 4; "Tricks" section 4:
+ * kernels measured on the real, small-batch workload).
+ *   x, wr, br          as moe_route;  w13_q, w13_s, w2_q, w2_s as
+ *                      moe_expert_mlp (flags: 0 or MOE_MLP_WEIGHTS_PACKED)
+ *   topk_ids, topk_w, counts, offsets, sorted_pairs, pair_pos
+ *                      written as moe_route writes them
+ *   out                [T, D] bf16 bits (written)
+ *   ws, ws_bytes       workspace of at least moe_layer_decode_workspace_size
+ *                      bytes whose first 256 bytes (the control block) were
+ *                      zeroed by moe_layer_decode_init; every successful call
+ *                      leaves them so.  Calls that overlap on one workspace
+ *                      race.
+ * Preconditions: as moe_route and moe_expert_mlp, plus T <= 64,
+ * T * E <= 8192 and a shape the streaming kernels take (D <= 3840,
+ * F <= 2944 for packed codes; D, F <= 4096).
+ * Device-side waits are bounded: if one gives up (a launch whose blocks
+ * could not all make progress), the call's outputs are invalid, an error is
+ * recorded in the control block (read with moe_layer_decode_error), all
+ * later kernels of the call stay in bounds, and the workspace must be
+ * initialised again before the next call.
+ * Errors: MOE_ERR_SHAPE, MOE_ERR_NULL, MOE_ERR_WORKSPACE, MOE_ERR_ENUM,
+ * MOE_ERR_ALIGN, MOE_ERR_DEVICE, MOE_ERR_HIP.
+ *
+ * moe_layer_decode_init -- zero the control block (enqueued on stream).
+ * moe_layer_decode_ex -- the same with spin_limit (polls per device-side
+ * wait, about 0.1 us apart; moe_layer_decode uses 1 << 20) and optional
+ * stage events as for moe_expert_mlp_ex (before the fused launch, after it,
+ * after the down kernel, after the combine).
+ * moe_layer_decode_error -- wait for `stream`, then store the control
+ * block's error word in *error (0: no wait gave up since the last init).
+ */
+MOE_API size_t moe_layer_decode_workspace_size(int32_t T, int32_t D, int32_t F, int32_t E,
+                                               int32_t k);
+MOE_API moe_status_t moe_layer_decode_init(void *ws, size_t ws_bytes, hipStream_t stream);
+MOE_API moe_status_t moe_layer_decode(const uint16_t *x, const float *wr, const float *br,
+                                      const uint8_t *w13_q, const uint8_t *w13_s,
+                                      const uint8_t *w2_q, const uint8_t *w2_s, int32_t T,
+                                      int32_t D, int32_t F, int32_t E, int32_t k,
+                                      int32_t *topk_ids, float *topk_w, int32_t *counts,
+                                      int32_t *offsets, int32_t *sorted_pairs,
+                                      int32_t *pair_pos, uint16_t *out, void *ws,
+                                      size_t ws_bytes, int flags, hipStream_t stream);
+MOE_API moe_status_t moe_layer_decode_ex(const uint16_t *x, const float *wr, const float *br,
+                                         const uint8_t *w13_q, const uint8_t *w13_s,
+                                         const uint8_t *w2_q, const uint8_t *w2_s, int32_t T,
+                                         int32_t D, int32_t F, int32_t E, int32_t k,
+                                         int32_t *topk_ids, float *topk_w, int32_t *counts,
+                                         int32_t *offsets, int32_t *sorted_pairs,
+                                         int32_t *pair_pos, uint16_t *out, void *ws,
+                                         size_t ws_bytes, int flags, int32_t spin_limit,
+                                         hipEvent_t *stage_events, hipStream_t stream);
+MOE_API moe_status_t moe_layer_decode_error(const void *ws, int32_t *error,
+                                            hipStream_t stream);
 
 /*
  * moe_expert_mlp_noalloc -- moe_expert_mlp_ex without a workspace argument

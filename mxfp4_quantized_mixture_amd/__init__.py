@@ -34,7 +34,7 @@ __all__ = ["mxfp4_quantize", "mxfp4_dequantize", "mxfp4_pack", "moe_route", "moe
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 NOALLOC_SCRATCH_BYTES = 16 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 SCALE_FLOOR_DIV6 = 0
 SCALE_OCP = 1
@@ -103,6 +103,18 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_mlp_bf16_ex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                              P, P, sz, P, P]
         L.moe_expert_mlp_bf16_ex.restype = ctypes.c_int
+        L.moe_layer_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_layer_decode_workspace_size.restype = sz
+        L.moe_layer_decode_init.argtypes = [P, sz, P]
+        L.moe_layer_decode_init.restype = ctypes.c_int
+        L.moe_layer_decode.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                       P, P, P, P, P, P, P, P, sz, ctypes.c_int, P]
+        L.moe_layer_decode.restype = ctypes.c_int
+        L.moe_layer_decode_ex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                          P, P, P, P, P, P, P, P, sz, ctypes.c_int, i32, P, P]
+        L.moe_layer_decode_ex.restype = ctypes.c_int
+        L.moe_layer_decode_error.argtypes = [P, P, P]
+        L.moe_layer_decode_error.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -348,6 +360,92 @@ def moe_expert_mlp_bf16(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, ro
         _dev(routing.pair_pos, "pair_pos", torch.int32), T, D, F, E, k,
         _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), ev, _stream(x.device)))
     return out
+
+
+DECODE_SPIN_LIMIT = 1 << 20
+
+
+def decode_workspace(T: int, D: int, F: int, E: int, k: int, device) -> torch.Tensor:
+    """Workspace of moe_layer_decode, its control block initialised."""
+    n = lib().moe_layer_decode_workspace_size(T, D, F, E, k)
+    if n == 0:
+        raise MoEError("moe_layer_decode_workspace_size", 2)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    decode_init(ws)
+    return ws
+
+
+def decode_init(ws: torch.Tensor) -> None:
+    _check("moe_layer_decode_init", lib().moe_layer_decode_init(
+        _dev(ws, "ws"), ws.numel(), _stream(ws.device)))
+
+
+def decode_error(ws: torch.Tensor) -> int:
+    """The control block's error word (waits for the current stream)."""
+    v = ctypes.c_int32(-1)
+    _check("moe_layer_decode_error", lib().moe_layer_decode_error(
+        _dev(ws, "ws"), ctypes.byref(v), _stream(ws.device)))
+    return v.value
+
+
+def moe_layer_decode(x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None,
+                     weights: ExpertWeights, k: int, out: torch.Tensor | None = None,
+                     routing: Routing | None = None, ws: torch.Tensor | None = None,
+                     events=None, spin_limit: int = DECODE_SPIN_LIMIT):
+    """Route + experts of a decode-sized batch with the routing fused into the
+    gate/up weight stream.  Returns (out, routing)."""
+    T, D = x.shape
+    E, F = weights.E, weights.F
+    if weights.D != D:
+        raise ValueError("expert weights do not match d_model")
+    out = out if out is not None else torch.empty(T, D, dtype=torch.bfloat16, device=x.device)
+    r = routing if routing is not None else alloc_routing(T, E, k, x.device)
+    ws = ws if ws is not None else decode_workspace(T, D, F, E, k, x.device)
+    ev = None if events is None else _event_array(events)
+    _check("moe_layer_decode", lib().moe_layer_decode_ex(
+        _dev(x, "x", torch.bfloat16), _dev(wr, "wr", torch.float32),
+        None if br is None else _dev(br, "br", torch.float32),
+        _dev(weights.w13_q, "w13_q", torch.uint8), _dev(weights.w13_s, "w13_s", torch.uint8),
+        _dev(weights.w2_q, "w2_q", torch.uint8), _dev(weights.w2_s, "w2_s", torch.uint8),
+        T, D, F, E, k, _dev(r.ids, "ids"), _dev(r.weights, "weights"), _dev(r.counts, "counts"),
+        _dev(r.offsets, "offsets"), _dev(r.sorted_pairs, "sorted_pairs"),
+        _dev(r.pair_pos, "pair_pos"), _dev(out, "out", torch.bfloat16), _dev(ws, "ws"),
+        ws.numel(), weights.algo_flags, spin_limit, ev, _stream(x.device)))
+    return out, r
+
+
+class PreparedDecodeLayer:
+    """moe_layer_decode with every C-ABI argument marshalled once (the
+    decode counterpart of PreparedLayer: calling it re-issues one C call)."""
+
+    def __init__(self, x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None,
+                 weights: ExpertWeights, k: int, out: torch.Tensor, routing: Routing,
+                 ws: torch.Tensor, stream=None):
+        T, D = x.shape
+        E, F = weights.E, weights.F
+        self.L = lib()
+        st = (stream or torch.cuda.current_stream(x.device)).cuda_stream
+        self._keep = (x, wr, br, weights, out, routing, ws)
+        self.head = (
+            _dev(x, "x", torch.bfloat16), _dev(wr, "wr", torch.float32),
+            None if br is None else _dev(br, "br", torch.float32),
+            _dev(weights.w13_q, "w13_q", torch.uint8), _dev(weights.w13_s, "w13_s", torch.uint8),
+            _dev(weights.w2_q, "w2_q", torch.uint8), _dev(weights.w2_s, "w2_s", torch.uint8),
+            T, D, F, E, k, _dev(routing.ids, "ids"), _dev(routing.weights, "weights"),
+            _dev(routing.counts, "counts"), _dev(routing.offsets, "offsets"),
+            _dev(routing.sorted_pairs, "sorted_pairs"), _dev(routing.pair_pos, "pair_pos"),
+            _dev(out, "out", torch.bfloat16), _dev(ws, "ws"), ws.numel(), weights.algo_flags,
+            DECODE_SPIN_LIMIT)
+        self.stream = st
+
+    @staticmethod
+    def event_array(events) -> ctypes.Array:
+        return _event_array(events)
+
+    def __call__(self, event_array=None) -> None:
+        s = self.L.moe_layer_decode_ex(*self.head, event_array, self.stream)
+        if s:
+            raise MoEError("moe_layer_decode", s)
 
 
 class MoELayer:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
 SOURCES = ["quantize.hip", "route.hip", "expert_mlp.hip", "expert_gemm.hip", "expert_bf16.hip",
-           "api.hip"]
+           "decode.hip", "api.hip"]
 PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -240,6 +240,69 @@ moe_status_t moe_expert_mlp_bf16(const uint16_t* x, const uint16_t* w13, const u
                                   E, k, out, ws, ws_bytes, nullptr, stream);
 }
 
+size_t moe_layer_decode_workspace_size(int32_t T, int32_t D, int32_t F, int32_t E, int32_t k) {
+    if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0) return 0;
+    const moe::DecodePlan p = moe::plan_decode(T, D, F, E, k);
+    return p.ok ? p.ws_bytes : 0;
+}
+
+moe_status_t moe_layer_decode_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws) return MOE_ERR_NULL;
+    if (ws_bytes < moe::kDecodeCtlBytes) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
+    return hip_status(moe::decode_init(ws, stream));
+}
+
+moe_status_t moe_layer_decode_ex(const uint16_t* x, const float* wr, const float* br,
+                                 const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                                 const uint8_t* w2_s, int32_t T, int32_t D, int32_t F, int32_t E,
+                                 int32_t k, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                                 uint16_t* out, void* ws, size_t ws_bytes, int flags,
+                                 int32_t spin_limit, hipEvent_t* stage_events,
+                                 hipStream_t stream) {
+    if (flags != 0 && flags != MOE_MLP_WEIGHTS_PACKED) return MOE_ERR_ENUM;
+    if (!route_shape_ok(T, D, E, k) || F < 32 || F % 32 != 0 || spin_limit < 0)
+        return MOE_ERR_SHAPE;
+    const moe::DecodePlan plan = moe::plan_decode(T, D, F, E, k);
+    const bool packed = flags == MOE_MLP_WEIGHTS_PACKED;
+    if (!plan.ok || (packed && !plan.mlp.packed_ok)) return MOE_ERR_SHAPE;
+    if (!x || !wr || !w13_q || !w13_s || !w2_q || !w2_s || !topk_ids || !topk_w || !counts ||
+        !offsets || !sorted_pairs || !pair_pos || !out)
+        return MOE_ERR_NULL;
+    if (!ws || ws_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(wr) || !aligned16(w13_q) || !aligned16(w13_s) ||
+        !aligned16(w2_q) || !aligned16(w2_s) || !aligned16(out) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
+    return hip_status(moe::launch_decode(plan, packed, x, wr, br, w13_q, w13_s, w2_q, w2_s,
+                                         topk_ids, topk_w, counts, offsets, sorted_pairs,
+                                         pair_pos, out, ws, spin_limit, stage_events, stream));
+}
+
+moe_status_t moe_layer_decode(const uint16_t* x, const float* wr, const float* br,
+                              const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                              const uint8_t* w2_s, int32_t T, int32_t D, int32_t F, int32_t E,
+                              int32_t k, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                              uint16_t* out, void* ws, size_t ws_bytes, int flags,
+                              hipStream_t stream) {
+    return moe_layer_decode_ex(x, wr, br, w13_q, w13_s, w2_q, w2_s, T, D, F, E, k, topk_ids,
+                               topk_w, counts, offsets, sorted_pairs, pair_pos, out, ws, ws_bytes,
+                               flags, 1 << 20, nullptr, stream);
+}
+
+moe_status_t moe_layer_decode_error(const void* ws, int32_t* error, hipStream_t stream) {
+    if (!ws || !error) return MOE_ERR_NULL;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if (const moe_status_t d = check_device(stream)) return d;
+    const int32_t* word = static_cast<const int32_t*>(ws) + moe::kDecodeCtlErr;
+    hipError_t er = hipMemcpyAsync(error, word, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (er == hipSuccess) er = hipStreamSynchronize(stream);
+    return hip_status(er);
+}
+
 moe_status_t moe_expert_mlp_noalloc(const uint16_t* x, const uint8_t* w13_q,
                                     const uint8_t* w13_s, const uint8_t* w2_q,
                                     const uint8_t* w2_s, const float* topk_w,

@@ -64,6 +64,13 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
                            const int32_t* offsets, const int32_t* sorted, float* y, char* base,
                            hipEvent_t* events, hipStream_t stream);
 
+// the streaming down kernel alone (h fp32 [P, F] -> y fp32 [P, D]), and the
+// streaming gate/up kernel's blocks per expert (expert_mlp.hip)
+hipError_t launch_stream_down(const MlpPlan& p, bool packed, const float* h, const uint8_t* w2q,
+                              const uint8_t* w2s, const int32_t* offsets, const int32_t* sorted,
+                              float* y, hipStream_t stream);
+int stream_blocks_gate_up(const MlpPlan& p);
+
 // out[t] = bf16(sum_j topk_w[t, j] y[pos[t k + j]]), slots in order
 // (expert_mlp.hip); events, if given, are recorded as stage events 2 and 3
 hipError_t launch_combine_rows(int T, int D, int k, const float* y, const float* topk_w,
@@ -77,5 +84,28 @@ hipError_t launch_mlp_bf16(int T, int D, int F, int E, int k, const uint16_t* x,
                            const uint16_t* w13, const uint16_t* w2, const float* topk_w,
                            const int32_t* offsets, const int32_t* sorted, const int32_t* pos,
                            uint16_t* out, void* ws, hipEvent_t* events, hipStream_t stream);
+
+// Fused decode front (decode.hip): router and gate/up weight stream in one
+// launch, then the streaming down kernel and the combine.  Workspace: a
+// 256-byte control block (zeroed once by decode_init), the router's partial
+// logits, then the streaming path's y and h.
+struct DecodePlan {
+    RoutePlan route;
+    MlpPlan mlp;
+    bool ok;                 // shape taken (T <= 64, T E <= 8192, streaming shapes)
+    int router_blocks;       // router tiles (one per block)
+    int gate_up_bpe;         // gate/up blocks per expert
+    size_t off_partials, off_mlp, ws_bytes;
+};
+DecodePlan plan_decode(int T, int D, int F, int E, int k);
+hipError_t decode_init(void* ws, hipStream_t stream);
+hipError_t launch_decode(const DecodePlan& p, bool packed, const uint16_t* x, const float* wr,
+                         const float* br, const uint8_t* w13q, const uint8_t* w13s,
+                         const uint8_t* w2q, const uint8_t* w2s, int32_t* ids, float* w,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                         uint16_t* out, void* ws, int spin_limit, hipEvent_t* events,
+                         hipStream_t stream);
+constexpr size_t kDecodeCtlBytes = 256;
+constexpr int kDecodeCtlErr = 3;      // int index of the sticky error word in the control block
 
 }  // namespace moe

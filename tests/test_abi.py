@@ -36,7 +36,9 @@ def test_header_declares_the_boundary():
             "moe_route_workspace_size",
             "moe_expert_mlp_workspace_size", "moe_status_string", "mxfp4_dequantize",
             "moe_abi_version", "moe_expert_mlp_bf16", "moe_expert_mlp_bf16_ex",
-            "moe_expert_mlp_bf16_workspace_size"} <= names
+            "moe_expert_mlp_bf16_workspace_size", "moe_layer_decode", "moe_layer_decode_ex",
+            "moe_layer_decode_init", "moe_layer_decode_error",
+            "moe_layer_decode_workspace_size"} <= names
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -79,7 +81,7 @@ def test_status_strings(L):
     assert len(names) == 7
     assert b"gfx950" in L.moe_status_string(DEVICE)
     assert L.moe_status_string(99) == b"unknown status"
-    assert L.moe_abi_version() == 3 == moe.ABI_VERSION
+    assert L.moe_abi_version() == 4 == moe.ABI_VERSION
 
 
 def test_header_status_codes_match():
@@ -230,6 +232,38 @@ def test_bf16_mlp_workspace_and_validation(L):
                                  FAKE, FAKE, 1 << 20, None) == SHAPE
 
 
+def _decode(L, T=8, D=64, F=64, E=4, k=2, out=FAKE, ws_bytes=None, flags=0, spin=1000,
+            x=FAKE):
+    if ws_bytes is None:
+        ws_bytes = L.moe_layer_decode_workspace_size(T, D, F, E, k) or 1 << 20
+    return L.moe_layer_decode_ex(x, FAKE, None, FAKE, FAKE, FAKE, FAKE, T, D, F, E, k, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, out, FAKE, ws_bytes, flags, spin,
+                                 None, None)
+
+
+def test_decode_workspace_and_validation(L):
+    T, D, F, E, k = 32, 2880, 2880, 32, 4
+    n = L.moe_layer_decode_workspace_size(T, D, F, E, k)
+    assert n >= 256 + 4 * T * k * (D + F)                     # control block, y, fp32 h
+    assert L.moe_layer_decode_workspace_size(65, 64, 64, 4, 2) == 0      # T > 64
+    assert L.moe_layer_decode_workspace_size(64, 64, 64, 256, 2) == 0    # T E > 8192
+    assert L.moe_layer_decode_workspace_size(8, 64, 48, 4, 2) == 0       # F % 32
+    assert L.moe_layer_decode_workspace_size(8, 64, 4160, 4, 2) == 0     # streaming LDS budget
+    assert _decode(L, flags=3) == ENUM
+    assert _decode(L, flags=moe.MLP_STREAM) == ENUM                      # only the packed flag
+    assert _decode(L, T=65) == SHAPE
+    assert _decode(L, F=40) == SHAPE
+    assert _decode(L, spin=-1) == SHAPE
+    assert _decode(L, D=96, flags=moe.MLP_WEIGHTS_PACKED) == SHAPE       # packed needs D % 64
+    assert _decode(L, out=None) == NULL
+    assert _decode(L, x=None) == NULL
+    assert _decode(L, ws_bytes=100) == WS
+    assert _decode(L, x=FAKE + 8) == ALIGN
+    assert L.moe_layer_decode_init(None, 1024, None) == NULL
+    assert L.moe_layer_decode_init(FAKE, 16, None) == WS
+    assert L.moe_layer_decode_error(FAKE, None, None) == NULL
+
+
 def _gpu_present():
     import torch
     return torch.cuda.is_available()
@@ -249,6 +283,8 @@ def test_valid_calls_without_a_gfx950_return_device_error(L):
     assert _mlp_ex(L, moe.MLP_GROUPED_GEMM) == DEVICE
     assert _mlp_ex(L, moe.MLP_AUTO, D=3904) == DEVICE           # taken by the grouped GEMM
     assert _bf16(L) == DEVICE
+    assert _decode(L) == DEVICE
+    assert L.moe_layer_decode_init(FAKE, 1024, None) == DEVICE
     # argument errors still win over the device check
     assert _mlp(L, F=40) == SHAPE
     assert _bf16(L, F=40) == SHAPE
