@@ -257,8 +257,9 @@ __device__ inline void scatter_chunk(const int* ids_lds, int npairs, int pair_ba
     }
 }
 
-// Few tokens (T <= kSmallTokens, T E <= kSmallLogits): one block of 16
-// wavefronts does the whole routing in one launch.
+// Few tokens (T <= kSmallTokens, T E <= kSmallLogits): one block of NW
+// wavefronts (16 in route_small_kernel, 8 in the fused decode front) does
+// the whole routing.
 //  1. Sum the router slices of every (token, expert) logit into LDS, 16
 //     slice loads in flight per thread (16 slices of one logit, or 4 slices
 //     of four logits when S <= 4); rows are padded to E + 1 floats so that
@@ -266,7 +267,7 @@ __device__ inline void scatter_chunk(const int* ids_lds, int npairs, int pair_ba
 //  2. Top-k with one lane per token: wavefront w keeps the best (logit, id)
 //     of its slice of experts in registers (insertion into a sorted list of
 //     k rounded up to a power of two; larger logit first, then lower id), and
-//     the 16 lists are merged pairwise through LDS (16 -> 8 -> 4 -> 2 -> 1).
+//     the NW lists are merged pairwise through LDS (16 -> 8 -> 4 -> 2 -> 1).
 //     The order of the selections is the same total order as repeated
 //     argmax.
 //  3. Softmax over the k, histogram, scan and stable scatter.
