@@ -285,18 +285,20 @@ def run_layer_bf16(cfg, steps, warmup, seed, moe, torch, dev):
     gu_bytes = touched * 2 * F * D * 2 + 2 * cfg.T * D
     dn_bytes = touched * D * F * 2
 
-    def hbm(bytes_, ms, kernel):
+    def hbm(bytes_, ms, kernel, traffic):
         a = bytes_ / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": a / HBM_PEAK_GBS, "kernel": kernel, "algorithmic_per_launch": bytes_,
-                "avg_launch_ms": ms}
+                "frac": a / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
+                "algorithmic_per_launch": bytes_, "avg_launch_ms": ms}
 
     ms = total_ms / steps
     return {"workload": cfg.description + ", bf16 expert weights", "expert_weights": "bf16",
             "tokens_per_s": cfg.T / (ms * 1e-3), "ms_per_step": ms, "steps": steps,
             "warmup": warmup, "stage_ms": st, "touched_experts": touched,
-            "roofline": hbm(gu_bytes, st["gate_up"], "expert_bf16_kernel<gate_up>"),
-            "roofline_down": hbm(dn_bytes, st["down"], "expert_bf16_kernel<down>")}
+            "roofline": hbm(gu_bytes, st["gate_up"], "expert_bf16_kernel<gate_up>",
+                            read_traffic("gateup_bf16", cfg.name, "expert_bf16.hip", "bf16")),
+            "roofline_down": hbm(dn_bytes, st["down"], "expert_bf16_kernel<down>",
+                                 read_traffic("down_bf16", cfg.name, "expert_bf16.hip", "bf16"))}
 
 
 def run_layer_fused_decode(cfg, steps, warmup, seed, moe, torch, dev):
@@ -480,6 +482,9 @@ def main() -> int:
                          "workload's expert weights (W13 and W2)")
     ap.add_argument("--probes", action="store_true",
                     help="only run the achievable-peak probes (HBM read, matrix cores)")
+    ap.add_argument("--fused-decode", action="store_true",
+                    help="only run the workload through moe_layer_decode (routing fused into "
+                         "the gate/up weight stream; decode-sized workloads)")
     ap.add_argument("--bf16-weights", action="store_true",
                     help="only run the bf16-weight comparison path (moe_expert_mlp_bf16) on the "
                          "workload")
@@ -520,6 +525,13 @@ def main() -> int:
                           "results": q}), flush=True)
         return 0
 
+    if args.fused_decode:
+        r = run_layer_fused_decode(cfg, args.steps, args.warmup, args.seed, moe, torch, dev)
+        print(json.dumps({"metric": "MXFP4 MoE-layer tokens/s, fused decode entry point",
+                          "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "config": {"workload": cfg.description, "name": cfg.name},
+                          "fused_decode": r}), flush=True)
+        return 0
     if args.bf16_weights:
         r = run_layer_bf16(cfg, args.steps, args.warmup, args.seed, moe, torch, dev)
         print(json.dumps({"metric": "MXFP4 MoE-layer tokens/s, bf16-weight comparison path",
