@@ -39,6 +39,21 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// fp32 -> fp16 bits, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Scale exponent s of a group of values with largest magnitude m for fp16
+// storage as v 2^-s: m 2^-s in [2^14, 2^15) (s = 0 for m = 0), s clamped to
+// [-127, 128] so that s + 127 fits a byte.
+__device__ __forceinline__ int y_scale_exponent(float m) {
+    if (!(m > 0.f)) return 0;
+    const int e = __builtin_amdgcn_frexp_expf(m);      // m = f 2^e, f in [0.5, 1)
+    const int s = e - 15;                             // m 2^-s = f 2^15
+    return s < -127 ? -127 : (s > 128 ? 128 : s);
+}
+
 // E8M0 scale byte b (meaning 2^(b-127)) as the fp32 scale operand of the
 // v_cvt_scalef32_* conversions.  b = 0 is the fp32 denormal 2^-127.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restri
 //   gate/up: the gate and the up rows of one feature fragment (a block
 //            covers WR fragments: with WR = 4, two whole 64-feature steps of
 //            h); epilogue h = silu(g) * u -> fp6 term rows;
-//   down:    two output fragments (a block covers 2 WR); epilogue y (fp32).
+//   down:    two output fragments (a block covers 2 WR); epilogue y (fp16
+//            with a power-of-two scale per pair and 32-output fragment).
 // No two wavefronts load the same weights, and a wavefront without a live
 // fragment (the last column range of an odd count) skips its products.
 // The contraction runs in 64-wide steps: activation steps go global -> LDS
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     const uint8_t* __restrict__ bq, const int32_t* __restrict__ sorted, int k,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
-    uint8_t* __restrict__ hq, float* __restrict__ y) {
+    uint8_t* __restrict__ hq, uint16_t* __restrict__ y16, uint8_t* __restrict__ ys) {
     constexpr int NT = kFp6Terms;
     constexpr int NA = 2;                               // A fragments per wave
     constexpr int NB = kGemmRows / 32;                  // pair fragments per wave
@@ -467,21 +468,38 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
             }
         }
     } else {
+        // y in fp16 with one power-of-two scale per (pair, 32-output fragment):
+        // the fragment's largest magnitude m is brought into [2^14, 2^15) (an
+        // exact ldexp), so every value keeps fp16's 11-bit precision relative to
+        // m (those more than 24 binades below m fall into fp16's subnormals),
+        // and no y overflows or underflows whatever its range.  Lane (n, g) holds
+        // 16 of the fragment's 32 outputs of pair 32 j + n, lane (n, 1 - g) the
+        // other 16.
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             if (a >= wcnt) break;
             const int f = wf0 + a;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
+                float m = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(acc[a][j][i]));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const int s = y_scale_exponent(m);
                 const int r = 32 * j + n;
                 if (r < nvalid) {
                     // element i: output 32 f + 8 (i / 4) + 4 g + i % 4 of pair r
-                    float* orow = y + (size_t)(row0 + r) * NOUT + 32 * f + 4 * g;
+                    uint16_t* orow = y16 + (size_t)(row0 + r) * NOUT + 32 * f + 4 * g;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        *reinterpret_cast<f32x4_t*>(orow + 8 * w) =
-                            f32x4_t{acc[a][j][4 * w], acc[a][j][4 * w + 1], acc[a][j][4 * w + 2],
-                                    acc[a][j][4 * w + 3]};
+                    for (int w = 0; w < 4; ++w) {
+                        uint32_t h2[2];
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+                            h2[c] = f32_to_f16_bits(__builtin_ldexpf(acc[a][j][4 * w + 2 * c], -s)) |
+                                    (f32_to_f16_bits(__builtin_ldexpf(acc[a][j][4 * w + 2 * c + 1], -s)) << 16);
+                        *reinterpret_cast<u32x2_t*>(orow + 8 * w) = u32x2_t{h2[0], h2[1]};
+                    }
+                    if (g == 0) ys[(size_t)(row0 + r) * (NOUT / 32) + f] = (uint8_t)(s + 127);
                 }
             }
         }
@@ -527,7 +545,8 @@ size_t gemm_lds_bytes(int K, bool gate_up) {
 template <bool kGateUp, int WR, bool kPacked>
 static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t* sorted,
                               const uint8_t* wq, const uint8_t* ws, const int32_t* tiles,
-                              int K, int NOUT, uint8_t* hq, float* y, hipStream_t stream) {
+                              int K, int NOUT, uint8_t* hq, uint16_t* y16, uint8_t* ys,
+                              hipStream_t stream) {
     constexpr int kBlockFrags = kGateUp ? WR : 2 * WR;
     const int ntl = (NOUT / 32 + kBlockFrags - 1) / kBlockFrags;
     const size_t lds = gemm_lds_bytes(K, kGateUp);
@@ -539,13 +558,15 @@ static hipError_t launch_gemm(const MlpPlan& p, const uint8_t* bq, const int32_t
     }
     hipLaunchKernelGGL((expert_gemm_kernel<kGateUp, WR, kPacked>),
                        dim3((unsigned)gemm_grid(p.max_tiles, ntl)), dim3(64 * WR), lds, stream,
-                       bq, sorted, p.k, wq, ws, tiles, p.max_tiles, ntl, K, NOUT, p.F, hq, y);
+                       bq, sorted, p.k, wq, ws, tiles, p.max_tiles, ntl, K, NOUT, p.F, hq, y16,
+                       ys);
     return hipSuccess;
 }
 
 hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                           const int32_t* offsets, const int32_t* sorted, float* y, char* base,
+                           const int32_t* offsets, const int32_t* sorted, uint16_t* y16,
+                           uint8_t* ys, char* base,
                            hipEvent_t* events, hipStream_t stream) {
     uint8_t* xq = reinterpret_cast<uint8_t*>(base + p.off_xq);
     uint8_t* hq = reinterpret_cast<uint8_t*>(base + p.off_h);
@@ -561,18 +582,18 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
     }
     hipError_t er;
     er = packed ? launch_gemm<true, kGateUpWaves, true>(p, xq, sorted, w13q, w13s, tiles, p.D,
-                                                        p.F, hq, nullptr, stream)
+                                                        p.F, hq, nullptr, nullptr, stream)
                 : launch_gemm<true, kGateUpWaves, false>(p, xq, sorted, w13q, w13s, tiles, p.D,
-                                                         p.F, hq, nullptr, stream);
+                                                         p.F, hq, nullptr, nullptr, stream);
     if (er != hipSuccess) return er;
     if (events) {
         er = hipEventRecord(events[1], stream);
         if (er != hipSuccess) return er;
     }
     er = packed ? launch_gemm<false, kDownWaves, true>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D,
-                                                       nullptr, y, stream)
+                                                       nullptr, y16, ys, stream)
                 : launch_gemm<false, kDownWaves, false>(p, hq, nullptr, w2q, w2s, tiles, p.F, p.D,
-                                                        nullptr, y, stream);
+                                                        nullptr, y16, ys, stream);
     if (er != hipSuccess) return er;
     return hipGetLastError();
 }

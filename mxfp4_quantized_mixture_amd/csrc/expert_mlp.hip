@@ -77,6 +77,56 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
 }
 
+// The same combine over y stored in fp16 with a power-of-two scale per
+// (pair, 32-output fragment) (ys byte = s + 127, value = y16 2^s), as the
+// grouped GEMM's down kernel writes it.
+__global__ __launch_bounds__(256) void combine16_kernel(
+    const uint16_t* __restrict__ y16, const uint8_t* __restrict__ ys,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ pos, int T, int D, int k,
+    uint16_t* __restrict__ out) {
+    const int q = D / 4;
+    const int64_t n = (int64_t)T * q;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int t = (int)(i / q), d4 = (int)(i % q);
+        int pr[kCombineMaxK];
+        float wv[kCombineMaxK];
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+                pr[j] = pos[t * k + j];
+                wv[j] = topk_w[t * k + j];
+            }
+        }
+        u32x2_t v[kCombineMaxK];
+        int sc[kCombineMaxK];
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+                v[j] = *reinterpret_cast<const u32x2_t*>(y16 + (size_t)pr[j] * D + d4 * 4);
+                sc[j] = (int)ys[(size_t)pr[j] * (D / 32) + (d4 * 4) / 32] - 127;
+            }
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t bits = (v[j][c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+                    const float yv = __builtin_ldexpf(
+                        (float)__builtin_bit_cast(_Float16, (uint16_t)bits), sc[j]);
+                    acc[c] = __builtin_fmaf(wv[j], yv, acc[c]);
+                }
+            }
+        }
+        uint2 o;
+        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(out + (size_t)t * D + d4 * 4) = o;
+    }
+}
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kMaxStreamLds = 158 * 1024;   // of 160 KiB, leaving room for static LDS
@@ -103,9 +153,12 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     p.packed_ok = p.gemm_ok && p.stream_ok;
     p.max_tiles = gemm_max_tiles(T, E, k);
     p.off_y = 0;
+    // (the grouped GEMM stores y as fp16 plus a scale byte per 32 outputs in
+    // the same region: P D 2 + P D / 32 bytes)
+    p.off_ys = align256(P * D * sizeof(uint16_t));
     // h: fp32 [P, F] for the streaming kernels, fp6 term rows for the grouped
     // GEMM; one region sized for either
-    p.off_h = align256(P * D * sizeof(float));
+    p.off_h = align256(std::max(P * D * sizeof(float), p.off_ys + P * D / 32));
     size_t h_bytes = P * F * sizeof(float);
     if (p.gemm_ok) h_bytes = std::max(h_bytes, gemm_term_bytes((int)P, F));
     size_t end = align256(p.off_h + h_bytes);
@@ -132,6 +185,9 @@ static int stream_blocks_per_expert(int E, int ntiles) {
 static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
                                  const int32_t* pos, uint16_t* out, hipEvent_t* events,
                                  hipStream_t stream);
+static hipError_t launch_combine16(const MlpPlan& p, const uint16_t* y16, const uint8_t* ys,
+                                   const float* topk_w, const int32_t* pos, uint16_t* out,
+                                   hipEvent_t* events, hipStream_t stream);
 
 // One streaming pass: gate/up (kGateUp, K = D, F output rows per expert) or
 // down (K = F, D output rows), blocks sized by stream_blocks_per_expert.
@@ -170,10 +226,12 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
     char* base = static_cast<char*>(ws);
     float* y = reinterpret_cast<float*>(base + p.off_y);
     if (algo == 2 || (algo == 0 && p.gemm_auto)) {
+        uint16_t* y16 = reinterpret_cast<uint16_t*>(base + p.off_y);
+        uint8_t* ys = reinterpret_cast<uint8_t*>(base + p.off_ys);
         const hipError_t er = launch_mlp_gemm(p, packed, x, w13q, w13s, w2q, w2s, offsets, sorted,
-                                              y, base, events, stream);
+                                              y16, ys, base, events, stream);
         if (er != hipSuccess) return er;
-        return launch_combine(p, y, topk_w, pos, out, events, stream);
+        return launch_combine16(p, y16, ys, topk_w, pos, out, events, stream);
     }
     float* h = reinterpret_cast<float*>(base + p.off_h);
     if (events) {
@@ -198,6 +256,25 @@ static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* 
                                  const int32_t* pos, uint16_t* out, hipEvent_t* events,
                                  hipStream_t stream) {
     return launch_combine_rows(p.T, p.D, p.k, y, topk_w, pos, out, events, stream);
+}
+
+static hipError_t launch_combine16(const MlpPlan& p, const uint16_t* y16, const uint8_t* ys,
+                                   const float* topk_w, const int32_t* pos, uint16_t* out,
+                                   hipEvent_t* events, hipStream_t stream) {
+    if (events) {
+        const hipError_t er = hipEventRecord(events[2], stream);
+        if (er != hipSuccess) return er;
+    }
+    const int64_t n = (int64_t)p.T * (p.D / 4);
+    int64_t gb = (n + 255) / 256;
+    if (gb > 8192) gb = 8192;
+    hipLaunchKernelGGL(combine16_kernel, dim3((unsigned)gb), dim3(256), 0, stream, y16, ys, topk_w,
+                       pos, p.T, p.D, p.k, out);
+    if (events) {
+        const hipError_t er = hipEventRecord(events[3], stream);
+        if (er != hipSuccess) return er;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_combine_rows(int T, int D, int k, const float* y, const float* topk_w,

@@ -28,7 +28,8 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
                         int32_t* sorted, int32_t* pos, float* logits_out, void* ws,
                         hipStream_t stream);
 
-// Workspace of moe_expert_mlp: y (fp32 [P, D], both paths), h (fp32 [P, F]
+// Workspace of moe_expert_mlp: y (fp32 [P, D] for weight streaming; fp16
+// [P, D] plus a scale byte per 32 outputs for the grouped GEMM), h (fp32 [P, F]
 // for weight streaming, fp6 term rows for the grouped GEMM: one region),
 // then the grouped GEMM's x term rows and tile table.
 struct MlpPlan {
@@ -39,6 +40,7 @@ struct MlpPlan {
     bool packed_ok;      // packed weights accepted: both algorithms take the shape
     int max_tiles;       // upper bound of 128-pair tiles over all experts
     size_t off_y;
+    size_t off_ys;       // grouped GEMM: y as fp16 at off_y, its scale bytes here
     size_t off_h;
     size_t off_xq, off_tiles;                        // grouped GEMM: x terms, tile table
     size_t ws_bytes;
@@ -61,7 +63,8 @@ constexpr size_t kGemmMaxLds = 157 * 1024;    // of 160 KiB; the rest is static 
 constexpr int kGemmMaxContraction = 8192;      // D and F limit of the grouped GEMM
 hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, const uint8_t* w13q,
                            const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                           const int32_t* offsets, const int32_t* sorted, float* y, char* base,
+                           const int32_t* offsets, const int32_t* sorted, uint16_t* y16,
+                           uint8_t* ys, char* base,
                            hipEvent_t* events, hipStream_t stream);
 
 // the streaming down kernel alone (h fp32 [P, F] -> y fp32 [P, D]), and the

@@ -561,10 +561,16 @@ def test_grouped_gemm_tail_stages_repeatable(D, F):
         wss.append(ws)
     torch.cuda.synchronize()
     P = cfg.T * cfg.k
-    n = (P * D * 4 + 255) // 256 * 256 + P * (F // 64) * 160   # y, then h as fp6 term rows
+    a256 = lambda v: (v + 255) // 256 * 256
+    # what the grouped GEMM writes: y as fp16 [P, D], its scale bytes [P, D / 32],
+    # then h as fp6 term rows (160 bytes per 64 elements)
+    off_ys = a256(P * D * 2)
+    off_h = a256(max(P * D * 4, off_ys + P * D // 32))
+    regions = [(0, P * D * 2), (off_ys, off_ys + P * D // 32), (off_h, off_h + P * (F // 64) * 160)]
     for rep in range(1, 6):
         assert torch.equal(outs[rep].view(torch.int16), outs[0].view(torch.int16)), rep
-        assert torch.equal(wss[rep][:n], wss[0][:n]), rep
+        for a, b in regions:
+            assert torch.equal(wss[rep][a:b], wss[0][a:b]), (rep, a, b)
     check_layer(inp, what=cfg.name + "/grouped-gemm", algo=moe.MLP_GROUPED_GEMM)
 
 
