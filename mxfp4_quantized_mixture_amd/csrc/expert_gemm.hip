@@ -42,9 +42,14 @@ constexpr int kGemmRows = 128;      // routed pairs per tile: 4 fragments of 32
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kScaleIters = 8;      // weight-scale copy: K <= 64 lanes x 16 bytes x 8
 static_assert(64 * 16 * kScaleIters == kGemmMaxContraction, "scale copy covers every K");
-// LDS row pitch of a staged step: its 160 bytes plus a 16-byte pad unit (an
-// odd number of 16-byte units keeps the operand reads free of bank conflicts)
-constexpr int kStepPitch = kTermStep + 16;
+// LDS row pitch of a staged step: its 160 bytes, 10 units of 16 bytes.  Row
+// r's units are rotated by rot(r) = (r / 8) mod 2 (unit u at position
+// (u + rot(r)) mod 10): the 128-bit operand reads of 16 consecutive rows then
+// hit 16 different groups of 4 banks (with 64 banks of 4 bytes), as an odd
+// pitch with a pad unit would, without staging the pad.  (rot depends on the
+// lane only: row 32 j + n has rot (n / 8) mod 2.)
+constexpr int kStepPitch = kTermStep;
+__device__ __forceinline__ int row_rot(int r) { return (r >> 3) & 1; }
 // gate/up epilogue: h of the block's 128 pairs x 128 features in fp32, rows
 // of kHRow floats
 constexpr int kHRow = 132;
@@ -181,9 +186,8 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     constexpr int NB = kGemmRows / 32;                  // pair fragments per wave
     constexpr int kThreads = 64 * WR;
     constexpr int kBlockFrags = kGateUp ? WR : 2 * WR;  // output fragments per block
-    // LDS slot of one step: the 128 rows' step chunks, row pitch kStepPitch
-    // (11 units of 16 bytes: the staging copy and the operand reads, lanes
-    // n = 0..15 at units 11 n mod 16, are free of bank conflicts)
+    // LDS slot of one step: the 128 rows' step chunks, row pitch kStepPitch,
+    // units rotated per row (row_rot)
     constexpr int kSlotBytes = kGemmRows * kStepPitch;
     constexpr int kRowPieces = kStepPitch / 16;
     constexpr int kPieces = (kGemmRows * kRowPieces + kThreads - 1) / kThreads;
@@ -264,16 +268,18 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     uint8_t* dummy = lds + kBufs * kSlotBytes + (size_t)WR * NA * K + (wave & 7) * 1024;
     __syncthreads();
 
-    // Staging: piece p = tid + kThreads c (p < 128 kRowPieces) is 16-byte
-    // piece p % kRowPieces of row p / kRowPieces's step chunk, loaded straight
-    // into byte 16 p of the LDS slot (a wave's 64 pieces land contiguously at
-    // a wave-uniform destination); the pad unit repeats the chunk's last.
+    // Staging: LDS unit p = tid + kThreads c (p < 128 kRowPieces) of the slot
+    // is position p % kRowPieces of row p / kRowPieces, which holds unit
+    // (position - row_rot) mod 10 of that row's step chunk; the 16 bytes are
+    // loaded straight into byte 16 p of the slot (a wave's 64 pieces land
+    // contiguously at a wave-uniform destination).
     uint32_t gsrc[kPieces];                             // byte offsets in bq (< 4 GiB)
 #pragma unroll
     for (int c = 0; c < kPieces; ++c) {
         const int p = min(tid + kThreads * c, kGemmRows * kRowPieces - 1);
         const int r = p / kRowPieces;
-        const int piece = min(p - r * kRowPieces, kTermStep / 16 - 1);
+        const int q = p - r * kRowPieces + kRowPieces - row_rot(r);
+        const int piece = q >= kRowPieces ? q - kRowPieces : q;
         gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * piece);
     }
 
@@ -326,12 +332,14 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     };
     auto read_frag = [&](int buf, int j, int t, Frag& fr) {
         // this lane's row (pair 32 j + n) of the step: term t of block g as
-        // 16 bytes at 48 t + 16 g and 8 bytes at 48 t + 32 + 8 g; its scale
-        // byte 144 + 2 t + g
+        // 16 bytes (unit 3 t + g) and 8 bytes (half g of unit 3 t + 2); its
+        // scale byte 144 + 2 t + g (in unit 9); units at their rotated places
+        // (units 0 .. 8 move up by rot, unit 9 wraps to 0 when rot = 1)
+        const int rot16 = 16 * row_rot(n);
         const uint8_t* row = lds + buf * kSlotBytes + (32 * j + n) * kStepPitch;
-        fr.sw = reinterpret_cast<const uint32_t*>(row + 144)[t >> 1] >> (8 * g);
-        fr.lo = *reinterpret_cast<const u32x4_t*>(row + 48 * t + 16 * g);
-        fr.hi = *reinterpret_cast<const u32x2_t*>(row + 48 * t + 32 + 8 * g);
+        fr.sw = *reinterpret_cast<const uint32_t*>(row + (144 - 9 * rot16) + 4 * (t >> 1)) >> (8 * g);
+        fr.lo = *reinterpret_cast<const u32x4_t*>(row + rot16 + 48 * t + 16 * g);
+        fr.hi = *reinterpret_cast<const u32x2_t*>(row + rot16 + 48 * t + 32 + 8 * g);
     };
     auto mfma_frag = [&](const AStep& a_cur, int j, auto tc, const Frag& fr, const int (&as)[NA]) {
         constexpr int t = decltype(tc)::value;
