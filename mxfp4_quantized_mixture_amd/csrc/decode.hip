@@ -7,7 +7,7 @@
 // weights, though, do not depend on the routing: here the expert blocks issue
 // their first weight batches first and only then wait for the routing, so
 // the routing's latency overlaps the start of the weight stream (the pages
-// ask that kernels be judged on the real workload, batch size included:
+// ask that kernels be measured on the real workload, batch size included:
 // "Tricks from OpenAI gpt-oss", section 4).
 //
 // One launch, three roles by block index:

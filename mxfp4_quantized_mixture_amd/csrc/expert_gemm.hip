@@ -302,8 +302,10 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     auto load_act = [&](int i) {
         const uint32_t so = (uint32_t)min(i, S - 1) * kTermStep;
         uint8_t* slot = lds + (i & 1) * kSlotBytes;
-        // (a wave whose pieces lie past the slot, in the last round, loads
-        // a duplicate into its dummy area: no branches in the loop)
+        // (with 4 wavefronts the slot's 1280 pieces are exactly 5 rounds;
+        // with other block sizes a wave whose pieces lie past the slot, in
+        // the last round, loads a duplicate into its dummy area: no branches
+        // in the loop)
 #pragma unroll
         for (int c = 0; c < kPieces; ++c) {
             const bool real = kThreads * c + wave * 64 < kGemmRows * kRowPieces;
