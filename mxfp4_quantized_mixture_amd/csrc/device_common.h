@@ -18,6 +18,10 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(32 * sizeof(float)))) float f32x32_t;
 typedef __attribute__((__vector_size__(6 * sizeof(uint32_t)))) uint32_t u32x6_t;
+// (clang extended vectors: any length, sub-vectors by __builtin_shufflevector)
+typedef uint32_t u32v4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32v8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32v12_t __attribute__((ext_vector_type(12)));
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
 // Workgroup barrier ordering LDS accesses only.  __syncthreads() also
@@ -183,36 +187,34 @@ __device__ __forceinline__ void fp6_block_terms(float (&v)[32], u32x6_t (&codes)
     }
 }
 
-// One 64-element step of an fp6 term row (kTermStep bytes, as 40 dwords):
-// bytes 48 t + 16 h .. + 15 hold the first 16 code bytes of term t of the
-// step's block h (h = 0, 1), bytes 48 t + 32 + 8 h .. + 7 its last 8, byte
-// 144 + 2 t + h its E8M0 scale; bytes 150 .. 159 are zero.  A lane (n, g) of
-// the 32x32x64 product thus reads its term-t operand of row n as one 16-byte
-// and one 8-byte piece, and its scale from the dword at 144 + 4 (t / 2).
+// One 64-element step of an fp6 term row (kTermStep bytes, as 40 dwords),
+// block-major: the step's block h (h = 0, 1) owns the 80 bytes (5 units of
+// 16) at 80 h; in them, dwords 6 t .. 6 t + 5 hold the 24 code bytes of its
+// term t, dword 18 its three E8M0 scales (term t in byte t), dword 19 is
+// zero.  A lane (n, g) of the 32x32x64 product thus reads everything it
+// needs of row n -- three fp6 operands and their scales -- as the five
+// 16-byte units of block g.
 constexpr int kTermStep = 160;
-static_assert(kFp6Terms == 3 && 48 * kFp6Terms + 2 * kFp6Terms <= kTermStep, "term step layout");
+constexpr int kTermHalf = kTermStep / 2;
+static_assert(kFp6Terms == 3 && 24 * kFp6Terms + 4 <= kTermHalf && kTermHalf % 16 == 0,
+              "term step layout");
 
 __device__ __forceinline__ void fp6_encode_step(float (&v)[64], uint32_t (&out)[kTermStep / 4]) {
-    uint32_t sb[2][kFp6Terms];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float blk[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) blk[i] = v[32 * h + i];
         u32x6_t codes[kFp6Terms];
-        fp6_block_terms(blk, codes, sb[h]);
+        uint32_t sb[kFp6Terms];
+        fp6_block_terms(blk, codes, sb);
 #pragma unroll
-        for (int t = 0; t < kFp6Terms; ++t) {
+        for (int t = 0; t < kFp6Terms; ++t)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) out[12 * t + 4 * h + w] = codes[t][w];
-            out[12 * t + 8 + 2 * h] = codes[t][4];
-            out[12 * t + 9 + 2 * h] = codes[t][5];
-        }
+            for (int w = 0; w < 6; ++w) out[20 * h + 6 * t + w] = codes[t][w];
+        out[20 * h + 18] = sb[0] | (sb[1] << 8) | (sb[2] << 16);
+        out[20 * h + 19] = 0u;
     }
-    out[36] = sb[0][0] | (sb[1][0] << 8) | (sb[0][1] << 16) | (sb[1][1] << 24);
-    out[37] = sb[0][2] | (sb[1][2] << 8);
-    out[38] = 0u;
-    out[39] = 0u;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }

@@ -26,9 +26,19 @@
 //   C: element i = row 8 (i / 4) + 4 g + i % 4, column n.
 //
 // Activation term rows: a row of K elements (K % 64 == 0) is K / 64 steps of
-// kTermStep = 160 bytes in the layout fp6_encode_step writes: per step the
-// codes of its two 32-blocks' 3 terms, then their scale bytes, so staging one
-// step of one row is one contiguous copy.
+// kTermStep = 160 bytes in the layout fp6_encode_step writes: per step its
+// two 32-blocks one after the other, each as its 3 terms' codes and then
+// their scale bytes (80 bytes), so a lane's operands of a step are the 80
+// bytes of its block.  x is stored by token, row after row (the gate/up GEMM
+// gathers a tile's rows).  h, which the gate/up epilogue writes tile by tile,
+// is stored tile by tile, step-major within a tile: the tile whose n pairs
+// start at sorted row r0 owns chunks r0 S .. (r0 + n) S - 1, step s of its
+// row p is chunk r0 S + s n + p, and each chunk's 16-byte units are already
+// rotated as the LDS staging wants them (row_rot below).  The down GEMM thus
+// stages a step with contiguous 1 KiB loads; its loads for rows p >= n of a
+// short tile read the next chunks of the region (which holds 128 rows of
+// slack past its P rows): finite fp6 codes in product columns that are
+// never stored, and the products of one column do not involve the others.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -44,10 +54,10 @@ constexpr int kScaleIters = 8;      // weight-scale copy: K <= 64 lanes x 16 byt
 static_assert(64 * 16 * kScaleIters == kGemmMaxContraction, "scale copy covers every K");
 // LDS row pitch of a staged step: its 160 bytes, 10 units of 16 bytes.  Row
 // r's units are rotated by rot(r) = (r / 8) mod 2 (unit u at position
-// (u + rot(r)) mod 10): the 128-bit operand reads of 16 consecutive rows then
-// hit 16 different groups of 4 banks (with 64 banks of 4 bytes), as an odd
-// pitch with a pad unit would, without staging the pad.  (rot depends on the
-// lane only: row 32 j + n has rot (n / 8) mod 2.)
+// (u + rot(r)) mod 10): the 128-bit operand reads of 16 consecutive rows (one
+// unit each) then hit 16 different groups of 4 banks (with 64 banks of 4
+// bytes), as an odd pitch with a pad unit would, without staging the pad.
+// (rot depends on the lane only: row 32 j + n has rot (n / 8) mod 2.)
 constexpr int kStepPitch = kTermStep;
 __device__ __forceinline__ int row_rot(int r) { return (r >> 3) & 1; }
 // gate/up epilogue: h of the block's 128 pairs x 128 features in fp32, rows
@@ -182,6 +192,7 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int ntl, int K, int NOUT, int F,
     uint8_t* __restrict__ hq, uint16_t* __restrict__ y16, uint8_t* __restrict__ ys) {
     constexpr int NT = kFp6Terms;
+    static_assert(NT == 3, "the first fragment's products are written out for three terms");
     constexpr int NA = 2;                               // A fragments per wave
     constexpr int NB = kGemmRows / 32;                  // pair fragments per wave
     constexpr int kThreads = 64 * WR;
@@ -272,15 +283,20 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
     // is position p % kRowPieces of row p / kRowPieces, which holds unit
     // (position - row_rot) mod 10 of that row's step chunk; the 16 bytes are
     // loaded straight into byte 16 p of the slot (a wave's 64 pieces land
-    // contiguously at a wave-uniform destination).
+    // contiguously at a wave-uniform destination).  gate/up gathers the
+    // tile's x rows; down reads byte 16 p of the tile's h step run.
     uint32_t gsrc[kPieces];                             // byte offsets in bq (< 4 GiB)
 #pragma unroll
     for (int c = 0; c < kPieces; ++c) {
         const int p = min(tid + kThreads * c, kGemmRows * kRowPieces - 1);
-        const int r = p / kRowPieces;
-        const int q = p - r * kRowPieces + kRowPieces - row_rot(r);
-        const int piece = q >= kRowPieces ? q - kRowPieces : q;
-        gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * piece);
+        if constexpr (kGateUp) {
+            const int r = p / kRowPieces;
+            const int q = p - r * kRowPieces + kRowPieces - row_rot(r);
+            const int piece = q >= kRowPieces ? q - kRowPieces : q;
+            gsrc[c] = (uint32_t)((size_t)s_src[r] * RB + 16 * piece);
+        } else {
+            gsrc[c] = (uint32_t)((size_t)row0 * RB + 16 * p);
+        }
     }
 
     f32x16_t acc[NA][NB];
@@ -300,7 +316,7 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
 
     // step i's activation chunks -> LDS buffer i % 2 (steps clamped)
     auto load_act = [&](int i) {
-        const uint32_t so = (uint32_t)min(i, S - 1) * kTermStep;
+        const uint32_t so = (uint32_t)min(i, S - 1) * (kGateUp ? kTermStep : nvalid * kTermStep);
         uint8_t* slot = lds + (i & 1) * kSlotBytes;
         // (with 4 wavefronts the slot's 1280 pieces are exactly 5 rounds;
         // with other block sizes a wave whose pieces lie past the slot, in
@@ -324,29 +340,42 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
         for (int a = 0; a < NA; ++a)
             dst[a] = *reinterpret_cast<const u32x4_t*>(wq + (aoff[a] + (kPacked ? 1024u : 32u) * st));
     };
-    // Products of one step, software-pipelined over its NB x NT operand
-    // groups (pair fragment j, term t): group q + 1's B operand is read from
-    // LDS while group q's NA products run.
+    // Products of one step, software-pipelined over its NB pair fragments:
+    // fragment j + 1's B operands are read from LDS while fragment j's
+    // NT x NA products run.  A lane's operands of fragment j are the five
+    // units 5 g .. 5 g + 4 of its row (pair 32 j + n): dwords 6 t .. 6 t + 5
+    // the codes of term t, dword 18 the terms' scales (term t in byte t).
+    // The units sit at their rotated places, position (u + rot) mod 10:
+    // only unit 9 (g = 1, rot = 1) wraps round, to position 0.
+    // (held as one 12-dword and one 8-dword vector, so that each term's six
+    // dwords are consecutive registers that the loads write directly)
     struct Frag {
-        u32x4_t lo;
-        u32x2_t hi;
-        uint32_t sw;                                    // scale word, byte 2 (t % 2) selected
+        u32v12_t a;                                     // dwords 0 .. 11: terms 0, 1
+        u32v8_t b;                                      // dwords 12 .. 19: term 2, scales
     };
-    auto read_frag = [&](int buf, int j, int t, Frag& fr) {
-        // this lane's row (pair 32 j + n) of the step: term t of block g as
-        // 16 bytes (unit 3 t + g) and 8 bytes (half g of unit 3 t + 2); its
-        // scale byte 144 + 2 t + g (in unit 9); units at their rotated places
-        // (units 0 .. 8 move up by rot, unit 9 wraps to 0 when rot = 1)
-        const int rot16 = 16 * row_rot(n);
+    const int uoff = 16 * (5 * g + row_rot(n));
+    const int uoff4 = g & row_rot(n) ? 0 : uoff + 64;
+    auto read_frag = [&](int buf, int j, Frag& fr) {
         const uint8_t* row = lds + buf * kSlotBytes + (32 * j + n) * kStepPitch;
-        fr.sw = *reinterpret_cast<const uint32_t*>(row + (144 - 9 * rot16) + 4 * (t >> 1)) >> (8 * g);
-        fr.lo = *reinterpret_cast<const u32x4_t*>(row + rot16 + 48 * t + 16 * g);
-        fr.hi = *reinterpret_cast<const u32x2_t*>(row + rot16 + 48 * t + 32 + 8 * g);
+        const u32v4_t r0 = *reinterpret_cast<const u32v4_t*>(row + uoff);
+        const u32v4_t r1 = *reinterpret_cast<const u32v4_t*>(row + uoff + 16);
+        const u32v4_t r2 = *reinterpret_cast<const u32v4_t*>(row + uoff + 32);
+        const u32v4_t r3 = *reinterpret_cast<const u32v4_t*>(row + uoff + 48);
+        const u32v4_t r4 = *reinterpret_cast<const u32v4_t*>(row + uoff4);
+        const u32v8_t r01 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const u32v8_t r22 = __builtin_shufflevector(r2, r2, 0, 1, 2, 3, 0, 1, 2, 3);
+        fr.a = __builtin_shufflevector(r01, r22, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11);
+        fr.b = __builtin_shufflevector(r3, r4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto mfma_frag = [&](const AStep& a_cur, int j, auto tc, const Frag& fr, const int (&as)[NA]) {
         constexpr int t = decltype(tc)::value;
-        const i32x8_t b8 = {(int)fr.lo[0], (int)fr.lo[1], (int)fr.lo[2], (int)fr.lo[3],
-                            (int)fr.hi[0], (int)fr.hi[1], 0, 0};
+        i32x8_t b8;
+        if constexpr (t == 0)
+            b8 = i32x8_t{(int)fr.a[0], (int)fr.a[1], (int)fr.a[2], (int)fr.a[3], (int)fr.a[4], (int)fr.a[5], 0, 0};
+        else if constexpr (t == 1)
+            b8 = i32x8_t{(int)fr.a[6], (int)fr.a[7], (int)fr.a[8], (int)fr.a[9], (int)fr.a[10], (int)fr.a[11], 0, 0};
+        else
+            b8 = i32x8_t{(int)fr.b[0], (int)fr.b[1], (int)fr.b[2], (int)fr.b[3], (int)fr.b[4], (int)fr.b[5], 0, 0};
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             // (dead fragments: no products; the branch is uniform)
@@ -354,35 +383,39 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
                 const i32x8_t a8 = {(int)a_cur[a][0], (int)a_cur[a][1], (int)a_cur[a][2],
                                     (int)a_cur[a][3], 0, 0, 0, 0};
                 // cbsz = 4: A is fp4 (E2M1); blgp = 2: B is fp6 (E2M3);
-                // B scale = byte 2 (t % 2) of its (shifted) scale word
+                // B scale = byte t of the scale dword
                 acc[a][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a8, b8, acc[a][j], 4, 2, 0, as[a], 2 * (t & 1), (int)fr.sw);
+                    a8, b8, acc[a][j], 4, 2, 0, as[a], t, (int)fr.b[6]);
             }
         }
     };
     // the step in buffer buf with weights a_cur, step index st; after_first()
-    // runs once the first group's products are issued
+    // runs once the first term's products are issued
     auto compute_step = [&](int buf, int st, const AStep& a_cur, auto&& after_first) {
-        constexpr int kGroups = NB * NT;
         Frag fr[2];
         int as[NA];
 #pragma unroll
         for (int a = 0; a < NA; ++a) as[a] = my_sc[a * K + 2 * st];
-        read_frag(buf, 0, 0, fr[0]);
-        static_for<kGroups>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            constexpr int j = q / NT, t = q % NT;
-            if constexpr (q + 1 < kGroups) read_frag(buf, (q + 1) / NT, (q + 1) % NT, fr[(q + 1) & 1]);
+        read_frag(buf, 0, fr[0]);
+        static_for<NB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j + 1 < NB) read_frag(buf, j + 1, fr[(j + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            // (a pair fragment past the tile's pairs, as in an expert's last
-            // tile, has no products to compute: its results are never
-            // stored; the branch is uniform in the wavefront)
-            if (32 * j < nvalid) mfma_frag(a_cur, j, std::integral_constant<int, t>{}, fr[q & 1], as);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (q == 0) {
+            if constexpr (j == 0) {
+                // (every tile has a pair in its first fragment)
+                mfma_frag(a_cur, 0, std::integral_constant<int, 0>{}, fr[0], as);
+                __builtin_amdgcn_sched_barrier(0);
                 after_first();
                 __builtin_amdgcn_sched_barrier(0);
+                mfma_frag(a_cur, 0, std::integral_constant<int, 1>{}, fr[0], as);
+                mfma_frag(a_cur, 0, std::integral_constant<int, 2>{}, fr[0], as);
+            } else if (32 * j < nvalid) {
+                // (a pair fragment past the tile's pairs, as in an expert's
+                // last tile, has no products to compute: its results are
+                // never stored; the branch is uniform in the wavefront)
+                static_for<NT>([&](auto tc) { mfma_frag(a_cur, j, tc, fr[j & 1], as); });
             }
+            __builtin_amdgcn_sched_barrier(0);
         });
     };
 
@@ -439,8 +472,8 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
         // (wave w: features 32 w .. 32 w + 31, C element i of pair fragment
         // j = feature 8 (i / 4) + 4 g + i % 4 of pair 32 j + n), gathered in
         // LDS (free now), then one thread per (pair, 64-feature step) turns
-        // its 64 values into fp6 terms and writes the 160-byte step chunk of
-        // the pair's h row.
+        // its 64 values into fp6 terms and writes the pair's 160-byte step
+        // chunk into the tile's h run, units rotated.
         static_assert(WR % 2 == 0 && WR * 32 <= kHRow, "epilogue layout: whole 64-feature steps");
         __syncthreads();                                // every wave is done with the stage buffers
         float* hb = reinterpret_cast<float*>(lds);
@@ -458,7 +491,7 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
         }
         __syncthreads();
         const int nsteps = (fb - fa) / 2;               // F % 64 == 0: whole steps
-        const size_t RBh = (size_t)(F / 64) * kTermStep;
+        const int Sh = F / 64;
         for (int task = tid; task < kGemmRows * (WR / 2); task += kThreads) {
             const int p = task / (WR / 2), hs = task % (WR / 2);
             if (p < nvalid && hs < nsteps) {
@@ -470,11 +503,14 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
                 }
                 uint32_t out[kTermStep / 4];
                 fp6_encode_step(v, out);
-                uint8_t* o = hq + (size_t)(row0 + p) * RBh + (size_t)(fa / 2 + hs) * kTermStep;
+                uint8_t* o = hq + ((size_t)row0 * Sh + (size_t)(fa / 2 + hs) * nvalid + p) * kTermStep;
+                const int rot = row_rot(p);
 #pragma unroll
-                for (int w = 0; w < kTermStep / 16; ++w)
-                    *reinterpret_cast<u32x4_t*>(o + 16 * w) =
+                for (int w = 0; w < kRowPieces; ++w) {
+                    const int pos = w + rot < kRowPieces ? w + rot : w + rot - kRowPieces;
+                    *reinterpret_cast<u32x4_t*>(o + 16 * pos) =
                         u32x4_t{out[4 * w], out[4 * w + 1], out[4 * w + 2], out[4 * w + 3]};
+                }
             }
         }
     } else {
@@ -528,6 +564,10 @@ int gemm_max_tiles(int T, int E, int k) {
 
 size_t gemm_term_bytes(int rows, int K) {
     return (size_t)rows * (K / 64) * kTermStep;
+}
+
+size_t gemm_h_bytes(int64_t P, int F) {
+    return gemm_term_bytes((int)(P + kGemmRows), F);
 }
 
 // Blocks for up to max_tiles x ntl work items, a multiple of the XCD count.

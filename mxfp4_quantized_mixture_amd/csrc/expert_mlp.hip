@@ -138,11 +138,11 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     const size_t P = (size_t)T * k;
     // (the grouped GEMM addresses its buffers with 32-bit byte offsets)
     const size_t k4G = (size_t)1 << 32;
+    p.max_tiles = gemm_max_tiles(T, E, k);
     p.gemm_ok = D % 64 == 0 && F % 64 == 0 && D <= kGemmMaxContraction &&
                 F <= kGemmMaxContraction && gemm_lds_bytes(D, true) <= kGemmMaxLds &&
                 gemm_lds_bytes(F, false) <= kGemmMaxLds && gemm_term_bytes(T, D) < k4G &&
-                gemm_term_bytes((int)std::min(P, (size_t)1 << 30), F) < k4G &&
-                (size_t)E * F * D < k4G;
+                gemm_h_bytes((int64_t)std::min(P, (size_t)1 << 30), F) < k4G && (size_t)E * F * D < k4G;
     p.stream_ok = stream_lds_bytes(D, 2, 2) <= kMaxStreamLds &&
                   stream_lds_bytes(F, 3, 1) <= kMaxStreamLds && D <= 4096 && F <= 4096;
     // Weight streaming reads every touched expert's weights once per 16 of its
@@ -151,16 +151,16 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     // shape.
     p.gemm_auto = p.gemm_ok && (P >= (size_t)32 * E || !p.stream_ok);
     p.packed_ok = p.gemm_ok && p.stream_ok;
-    p.max_tiles = gemm_max_tiles(T, E, k);
     p.off_y = 0;
     // (the grouped GEMM stores y as fp16 plus a scale byte per 32 outputs in
     // the same region: P D 2 + P D / 32 bytes)
     p.off_ys = align256(P * D * sizeof(uint16_t));
-    // h: fp32 [P, F] for the streaming kernels, fp6 term rows for the grouped
-    // GEMM; one region sized for either
+    // h: fp32 [P, F] for the streaming kernels, fp6 term rows packed by tile
+    // (with 128 rows of slack) for the grouped GEMM; one region sized for
+    // either
     p.off_h = align256(std::max(P * D * sizeof(float), p.off_ys + P * D / 32));
     size_t h_bytes = P * F * sizeof(float);
-    if (p.gemm_ok) h_bytes = std::max(h_bytes, gemm_term_bytes((int)P, F));
+    if (p.gemm_ok) h_bytes = std::max(h_bytes, gemm_h_bytes((int64_t)P, F));
     size_t end = align256(p.off_h + h_bytes);
     if (p.gemm_ok) {
         p.off_xq = end;

@@ -57,6 +57,7 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
 
 // grouped-GEMM path (expert_gemm.hip)
 int gemm_max_tiles(int T, int E, int k);
+size_t gemm_h_bytes(int64_t P, int F);   // h term rows of the grouped GEMM, with slack
 size_t gemm_term_bytes(int rows, int K);
 size_t gemm_lds_bytes(int K, bool gate_up);
 constexpr size_t kGemmMaxLds = 157 * 1024;    // of 160 KiB; the rest is static LDS

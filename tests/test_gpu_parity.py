@@ -563,7 +563,7 @@ def test_grouped_gemm_tail_stages_repeatable(D, F):
     P = cfg.T * cfg.k
     a256 = lambda v: (v + 255) // 256 * 256
     # what the grouped GEMM writes: y as fp16 [P, D], its scale bytes [P, D / 32],
-    # then h as fp6 term rows (160 bytes per 64 elements)
+    # then h as fp6 term rows (160 bytes per 64 elements, packed tile by tile)
     off_ys = a256(P * D * 2)
     off_h = a256(max(P * D * 4, off_ys + P * D // 32))
     regions = [(0, P * D * 2), (off_ys, off_ys + P * D // 32), (off_h, off_h + P * (F // 64) * 160)]
