@@ -21,6 +21,8 @@ struct RoutePlan {
     int splits;        // slices of the router contraction (partial logits summed in order)
     int chunks;        // token chunks of the top-k / histogram pass
     size_t off_logits, off_chunk_counts, off_chunk_base, ws_bytes;
+    bool gemm_router;   // longer batches: router_gemm_kernel
+    int gemm_router_ne; // its 16-expert tiles per block (2 or 4)
 };
 RoutePlan plan_route(int T, int D, int E, int k);
 hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, const float* br,

@@ -9,7 +9,13 @@
 //
 // Kernels:
 //   router_logits_kernel   matrix-core logits (fp32 weights as 3 exact bf16
-//                          terms), split-K over wavefronts and blocks
+//                          terms), split-K over wavefronts and blocks: decode
+//                          batches (T <= 64) and contractions not a multiple
+//                          of 64
+//   router_gemm_kernel     longer batches: 32- or 64-expert x 256-token tiles
+//                          staged through LDS chunk by chunk (whole-line
+//                          loads, each weight split once per block), split-K
+//                          over blocks only
 //   route_topk_kernel      one wavefront per token: k rounds of wave-wide
 //                          DPP argmax, softmax over the k, per-chunk histogram
 //   route_finish_kernel    few pairs: histogram, scan and scatter in one block
@@ -26,6 +32,140 @@
 #include "route_device.h"
 
 namespace moe {
+
+// Router logits of longer batches.  Block (bx, by, bz) of 4 wavefronts:
+// experts 16 NE bx .. + 16 NE - 1, tokens 256 by .. 256 by + 255,
+// contraction chunks [c0, c1) of
+// 64 (slice bz of S; slice s writes P[s], slice 0 adds the bias).  Each
+// chunk of the fp32 weight rows (16 NE rows) and of x (256 rows) is loaded
+// with whole-line loads into registers one chunk ahead; the block then
+// splits the weights into their three exact bf16 terms (split3_bf16, the
+// terms router_logits_tile forms) and writes terms and x rows to LDS rows of
+// kRgPitch bytes (128 + 16: the 16-byte operand reads of 16 consecutive rows
+// then hit 16 different bank groups), each weight split once per block.
+// Wavefront w owns tokens 64 w .. 64 w + 63 against all the block's experts:
+// per 32-wide step NE x 4 tiles x 3 terms of 16x16x32 bf16 products,
+// C[expert][token] as in router_logits_tile.  Rows past E or T load clamped
+// rows; their results are not stored.
+constexpr int kRgK = 64, kRgPitch = 144, kRgTok = 256, kRgWaves = 4, kRgThreads = 64 * kRgWaves;
+template <int NE>
+struct RouterGemm {
+    static constexpr int kExp = 16 * NE;
+    static constexpr int kTT = kRgTok / 16 / kRgWaves;       // 16-token tiles per wave
+    static constexpr int kGroups = kExp * (kRgK / 8);        // 8-weight groups per chunk
+    static constexpr int kWPer = kGroups / kRgThreads;       // per thread
+    static constexpr int kXPer = kRgTok * (kRgK / 8) / kRgThreads;  // 16-byte x units per thread
+    static constexpr int kLds = (3 * kExp + kRgTok) * kRgPitch;
+    static_assert(kGroups % kRgThreads == 0, "even split");
+};
+
+template <int NE>
+__global__ __launch_bounds__(kRgThreads, 2) void router_gemm_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ br,
+    float* __restrict__ P, int T, int D, int E, int S) {
+    using G = RouterGemm<NE>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int e0 = blockIdx.x * G::kExp, t0 = blockIdx.y * kRgTok, sl = blockIdx.z;
+    const int nch = D / kRgK;
+    const int c0 = (int)((int64_t)nch * sl / S), c1 = (int)((int64_t)nch * (sl + 1) / S);
+    // weight group q = tid + 256 i: row q / 8, weights 8 (q % 8) .. + 7 of the
+    // chunk; x unit u = tid + 256 i: row u / 8, elements 8 (u % 8) .. + 7
+    int64_t wsrc[G::kWPer], xsrc[G::kXPer];
+    int wdst[G::kWPer], xdst[G::kXPer];
+#pragma unroll
+    for (int i = 0; i < G::kWPer; ++i) {
+        const int q = tid + kRgThreads * i, r = q / 8, c = q % 8;
+        wsrc[i] = (int64_t)min(e0 + r, E - 1) * D + 8 * c;
+        wdst[i] = r * kRgPitch + 16 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < G::kXPer; ++i) {
+        const int u = tid + kRgThreads * i, r = u / 8, c = u % 8;
+        xsrc[i] = (int64_t)min(t0 + r, T - 1) * D + 8 * c;
+        xdst[i] = (3 * G::kExp + r) * kRgPitch + 16 * c;
+    }
+    struct Stage {
+        float4 w[G::kWPer][2];
+        u32x4_t x[G::kXPer];
+    };
+    Stage sa;                                   // the next chunk, loaded during this one
+    auto load_chunk = [&](Stage& st, int ch) {
+        const int64_t k0 = (int64_t)ch * kRgK;
+#pragma unroll
+        for (int i = 0; i < G::kWPer; ++i) {
+            st.w[i][0] = *reinterpret_cast<const float4*>(wr + wsrc[i] + k0);
+            st.w[i][1] = *reinterpret_cast<const float4*>(wr + wsrc[i] + k0 + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < G::kXPer; ++i)
+            st.x[i] = *reinterpret_cast<const u32x4_t*>(x + xsrc[i] + k0);
+    };
+    constexpr int TT = G::kTT;
+    f32x4_t acc[NE][TT];
+#pragma unroll
+    for (int et = 0; et < NE; ++et)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc[et][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto run_chunk = [&](Stage& st, int ch) {
+        __syncthreads();                        // every wave is done with the previous chunk
+#pragma unroll
+        for (int i = 0; i < G::kWPer; ++i) {
+            const float w[8] = {st.w[i][0].x, st.w[i][0].y, st.w[i][0].z, st.w[i][0].w,
+                                st.w[i][1].x, st.w[i][1].y, st.w[i][1].z, st.w[i][1].w};
+            bf16x8_t t3[3];
+            split3_bf16(w, t3[0], t3[1], t3[2]);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                *reinterpret_cast<u32x4_t*>(lds + pl * G::kExp * kRgPitch + wdst[i]) =
+                    __builtin_bit_cast(u32x4_t, t3[pl]);
+        }
+#pragma unroll
+        for (int i = 0; i < G::kXPer; ++i) *reinterpret_cast<u32x4_t*>(lds + xdst[i]) = st.x[i];
+        __syncthreads();
+        if (ch + 1 < c1) load_chunk(st, ch + 1);
+#pragma unroll
+        for (int j = 0; j < kRgK / 32; ++j) {
+            bf16x8_t xb[TT];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                xb[tt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+                    lds + (3 * G::kExp + 16 * (TT * wave + tt) + m) * kRgPitch + 64 * j + 16 * g));
+#pragma unroll
+            for (int et = 0; et < NE; ++et) {
+                bf16x8_t wt[3];
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+                    wt[pl] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+                        lds + (pl * G::kExp + 16 * et + m) * kRgPitch + 64 * j + 16 * g));
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+                    acc[et][tt] = mfma_bf16(wt[0], xb[tt], acc[et][tt]);
+                    acc[et][tt] = mfma_bf16(wt[1], xb[tt], acc[et][tt]);
+                    acc[et][tt] = mfma_bf16(wt[2], xb[tt], acc[et][tt]);
+                }
+            }
+        }
+    };
+    if (c0 < c1) load_chunk(sa, c0);
+    for (int ch = c0; ch < c1; ++ch) run_chunk(sa, ch);
+    // lane (m, g) of tile (et, tt) holds experts e0 + 16 et + 4 g + r of token
+    // t0 + 16 (TT w + tt) + m
+    float* Ps = P + (int64_t)sl * T * E;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int t = t0 + 16 * (TT * wave + tt) + m;
+        if (t >= T) continue;
+#pragma unroll
+        for (int et = 0; et < NE; ++et)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = e0 + 16 * et + 4 * g + r;
+                if (e < E) Ps[(int64_t)t * E + e] = acc[et][tt][r] + ((br && sl == 0) ? br[e] : 0.f);
+            }
+    }
+}
 
 // Router logits kernel: one tile per block (see router_logits_tile).
 template <int TT, int NE, int KB, bool kPipe>
@@ -250,6 +390,8 @@ RoutePlan plan_route(int T, int D, int E, int k) {
     RoutePlan p{};
     p.T = T; p.D = D; p.E = E; p.k = k;
     p.token_tiles = T <= 64 ? 1 : 4;           // 16-token tiles per router block
+    // longer batches with whole 64-wide contraction chunks: router_gemm_kernel
+    p.gemm_router = T > 64 && D % kRgK == 0;
     // 16-expert tiles per router block: one for decode (latency: many small
     // blocks), several for long batches (each block reads its x rows once for
     // all of them)
@@ -261,7 +403,17 @@ RoutePlan plan_route(int T, int D, int E, int k) {
     // wavefront keeps at least one 32-column step
     const int want = T <= 64 ? 128 : 512;
     int S = (want + tiles - 1) / tiles;
-    const int max_s = (D / 32) / kRouterWaves;
+    int max_s = (D / 32) / kRouterWaves;
+    // router_gemm blocks of 256 tokens and 32 experts when there are at most
+    // 32, else 64 (measured: 128 experts x 128 tokens, which reads x once, and
+    // a second register stage were both slower)
+    p.gemm_router_ne = E <= 32 ? 2 : 4;
+    if (p.gemm_router) {
+        const int ge = 16 * p.gemm_router_ne;
+        const int gt = ((E + ge - 1) / ge) * ((T + kRgTok - 1) / kRgTok);
+        S = (want + gt - 1) / gt;
+        max_s = D / kRgK;                      // at least one chunk per slice
+    }
     if (S > max_s) S = max_s;
     if (S > 16) S = 16;
     p.splits = S < 1 ? 1 : S;
@@ -288,7 +440,17 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
     {
         const int et = 16 * p.expert_tiles, tt = 16 * p.token_tiles;
         const dim3 g((p.E + et - 1) / et, (p.T + tt - 1) / tt, p.splits);
-        if (p.token_tiles == 1)
+        if (p.gemm_router) {
+            const int ge = 16 * p.gemm_router_ne;
+            const dim3 gg((p.E + ge - 1) / ge, (p.T + kRgTok - 1) / kRgTok, p.splits);
+            constexpr size_t lds2 = RouterGemm<2>::kLds, lds4 = RouterGemm<4>::kLds;
+            if (p.gemm_router_ne == 2)
+                hipLaunchKernelGGL((router_gemm_kernel<2>), gg, dim3(kRgThreads), lds2, stream, x,
+                                   wr, br, P, p.T, p.D, p.E, p.splits);
+            else
+                hipLaunchKernelGGL((router_gemm_kernel<4>), gg, dim3(kRgThreads), lds4, stream, x,
+                                   wr, br, P, p.T, p.D, p.E, p.splits);
+        } else if (p.token_tiles == 1)
             hipLaunchKernelGGL((router_logits_kernel<1, 1, 4, false>), g, dim3(kRouterWaves * 64), 0,
                                stream, x, wr, br, P, p.T, p.D, p.E, p.splits);
         else if (p.expert_tiles == 2)

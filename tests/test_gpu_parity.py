@@ -215,9 +215,12 @@ def test_route_workloads(name, seed):
     check_route(MI.gen_x(cfg, seed), wr, b, cfg.k, "%s/seed%d" % (name, seed))
 
 
+# (T > 64 with D % 64 == 0 runs router_gemm_kernel: 32-expert blocks for E <= 32,
+# 64-expert blocks otherwise, ragged in tokens and experts; other shapes the
+# tile kernel)
 @pytest.mark.parametrize("T,D,E,k", [(1, 32, 1, 1), (1, 64, 8, 8), (200, 96, 16, 3),
                                      (130, 64, 256, 8), (65, 32, 5, 5), (4096, 128, 64, 4),
-                                     (333, 2880, 128, 4)])
+                                     (333, 2880, 128, 4), (300, 128, 33, 2), (700, 4096, 40, 4)])
 def test_route_shapes(T, D, E, k):
     rng = np.random.default_rng(T * 7 + E)
     x = MI.f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
