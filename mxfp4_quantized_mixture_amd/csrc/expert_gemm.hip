@@ -102,13 +102,52 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 rows -> fp6 term rows.  One thread per (row, 64-element step).
+// Tile table: expert e's pairs [offsets[e], offsets[e+1]) in tiles of
+// kGemmRows, experts in order.  tiles[2 i] = first sorted row of tile i,
+// tiles[2 i + 1] = e | rows << 16; tiles[2 max_tiles] = number of tiles.
+// Computed by one block of 256 threads (E <= 256).
+// ---------------------------------------------------------------------------
+__device__ void gemm_tile_table(const int32_t* __restrict__ offsets, int E, int max_tiles,
+                                int32_t* __restrict__ tiles) {
+    __shared__ int part[256];
+    const int e = threadIdx.x;
+    const int beg = e < E ? offsets[e] : 0;
+    const int ne = e < E ? offsets[e + 1] - beg : 0;
+    const int c = (ne + kGemmRows - 1) / kGemmRows;
+    part[e] = c;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {        // inclusive scan
+        const int v = e >= d ? part[e - d] : 0;
+        __syncthreads();
+        part[e] += v;
+        __syncthreads();
+    }
+    const int first = part[e] - c;
+    for (int j = 0; j < c && first + j < max_tiles; ++j) {
+        const int rows = min(kGemmRows, ne - j * kGemmRows);
+        tiles[2 * (first + j)] = beg + j * kGemmRows;
+        tiles[2 * (first + j) + 1] = e | (rows << 16);
+    }
+    if (e == 255) tiles[2 * max_tiles] = min(part[255], max_tiles);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 rows -> fp6 term rows, one thread per (row, 64-element step); the
+// grid's extra first block computes the tile table (one launch fewer; as the
+// first block dispatched it runs beside the conversion, not after it).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void split_terms_kernel(const uint16_t* __restrict__ src,
                                                           int rows, int K,
-                                                          uint8_t* __restrict__ tq) {
+                                                          uint8_t* __restrict__ tq,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E, int max_tiles,
+                                                          int32_t* __restrict__ tiles) {
+    if (blockIdx.x == 0) {
+        gemm_tile_table(offsets, E, max_tiles, tiles);
+        return;
+    }
     const int S = K / 64;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t idx = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)rows * S) return;
     const int row = (int)(idx / S), s = (int)(idx - (int64_t)row * S);
     const uint16_t* p = src + (size_t)row * K + (size_t)s * 64;
@@ -132,37 +171,6 @@ __global__ __launch_bounds__(256) void split_terms_kernel(const uint16_t* __rest
     for (int w = 0; w < kTermStep / 16; ++w)
         *reinterpret_cast<u32x4_t*>(o + 16 * w) =
             u32x4_t{out[4 * w], out[4 * w + 1], out[4 * w + 2], out[4 * w + 3]};
-}
-
-// ---------------------------------------------------------------------------
-// Tile table: expert e's pairs [offsets[e], offsets[e+1]) in tiles of
-// kGemmRows, experts in order.  tiles[2 i] = first sorted row of tile i,
-// tiles[2 i + 1] = e | rows << 16; tiles[2 max_tiles] = number of tiles.
-// One block of 256 threads (E <= 256).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gemm_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int max_tiles,
-                                                         int32_t* __restrict__ tiles) {
-    __shared__ int part[256];
-    const int e = threadIdx.x;
-    const int beg = e < E ? offsets[e] : 0;
-    const int ne = e < E ? offsets[e + 1] - beg : 0;
-    const int c = (ne + kGemmRows - 1) / kGemmRows;
-    part[e] = c;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {        // inclusive scan
-        const int v = e >= d ? part[e - d] : 0;
-        __syncthreads();
-        part[e] += v;
-        __syncthreads();
-    }
-    const int first = part[e] - c;
-    for (int j = 0; j < c && first + j < max_tiles; ++j) {
-        const int rows = min(kGemmRows, ne - j * kGemmRows);
-        tiles[2 * (first + j)] = beg + j * kGemmRows;
-        tiles[2 * (first + j) + 1] = e | (rows << 16);
-    }
-    if (e == 255) tiles[2 * max_tiles] = min(part[255], max_tiles);
 }
 
 // ---------------------------------------------------------------------------
@@ -621,11 +629,9 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
     uint8_t* xq = reinterpret_cast<uint8_t*>(base + p.off_xq);
     uint8_t* hq = reinterpret_cast<uint8_t*>(base + p.off_h);
     int32_t* tiles = reinterpret_cast<int32_t*>(base + p.off_tiles);
-    hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(256), 0, stream, offsets, p.E,
-                       p.max_tiles, tiles);
     const int64_t nsplit = (int64_t)p.T * (p.D / 64);
-    hipLaunchKernelGGL(split_terms_kernel, dim3((unsigned)((nsplit + 255) / 256)), dim3(256), 0,
-                       stream, x, p.T, p.D, xq);
+    hipLaunchKernelGGL(split_terms_kernel, dim3((unsigned)((nsplit + 255) / 256 + 1)), dim3(256), 0,
+                       stream, x, p.T, p.D, xq, offsets, p.E, p.max_tiles, tiles);
     if (events) {
         const hipError_t er = hipEventRecord(events[0], stream);
         if (er != hipSuccess) return er;

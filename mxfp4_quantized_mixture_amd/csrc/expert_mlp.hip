@@ -79,16 +79,17 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 // The same combine over y stored in fp16 with a power-of-two scale per
 // (pair, 32-output fragment) (ys byte = s + 127, value = y16 2^s), as the
-// grouped GEMM's down kernel writes it.
+// grouped GEMM's down kernel writes it: eight outputs per thread (16-byte
+// loads and stores; the eight share one scale byte per slot).
 __global__ __launch_bounds__(256) void combine16_kernel(
     const uint16_t* __restrict__ y16, const uint8_t* __restrict__ ys,
     const float* __restrict__ topk_w, const int32_t* __restrict__ pos, int T, int D, int k,
     uint16_t* __restrict__ out) {
-    const int q = D / 4;
+    const int q = D / 8;
     const int64_t n = (int64_t)T * q;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int t = (int)(i / q), d4 = (int)(i % q);
+        const int t = (int)(i / q), d8 = (int)(i % q);
         int pr[kCombineMaxK];
         float wv[kCombineMaxK];
 #pragma unroll
@@ -98,21 +99,21 @@ __global__ __launch_bounds__(256) void combine16_kernel(
                 wv[j] = topk_w[t * k + j];
             }
         }
-        u32x2_t v[kCombineMaxK];
+        u32x4_t v[kCombineMaxK];
         int sc[kCombineMaxK];
 #pragma unroll
         for (int j = 0; j < kCombineMaxK; ++j) {
             if (j < k) {
-                v[j] = *reinterpret_cast<const u32x2_t*>(y16 + (size_t)pr[j] * D + d4 * 4);
-                sc[j] = (int)ys[(size_t)pr[j] * (D / 32) + (d4 * 4) / 32] - 127;
+                v[j] = *reinterpret_cast<const u32x4_t*>(y16 + (size_t)pr[j] * D + d8 * 8);
+                sc[j] = (int)ys[(size_t)pr[j] * (D / 32) + (d8 * 8) / 32] - 127;
             }
         }
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kCombineMaxK; ++j) {
             if (j < k) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < 8; ++c) {
                     const uint32_t bits = (v[j][c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
                     const float yv = __builtin_ldexpf(
                         (float)__builtin_bit_cast(_Float16, (uint16_t)bits), sc[j]);
@@ -120,10 +121,11 @@ __global__ __launch_bounds__(256) void combine16_kernel(
                 }
             }
         }
-        uint2 o;
-        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-        *reinterpret_cast<uint2*>(out + (size_t)t * D + d4 * 4) = o;
+        u32x4_t o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            o[c] = f32_to_bf16_rne(acc[2 * c]) | (f32_to_bf16_rne(acc[2 * c + 1]) << 16);
+        *reinterpret_cast<u32x4_t*>(out + (size_t)t * D + d8 * 8) = o;
     }
 }
 
@@ -265,7 +267,7 @@ static hipError_t launch_combine16(const MlpPlan& p, const uint16_t* y16, const 
         const hipError_t er = hipEventRecord(events[2], stream);
         if (er != hipSuccess) return er;
     }
-    const int64_t n = (int64_t)p.T * (p.D / 4);
+    const int64_t n = (int64_t)p.T * (p.D / 8);
     int64_t gb = (n + 255) / 256;
     if (gb > 8192) gb = 8192;
     hipLaunchKernelGGL(combine16_kernel, dim3((unsigned)gb), dim3(256), 0, stream, y16, ys, topk_w,
