@@ -411,10 +411,17 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (j == 0) {
                 // (every tile has a pair in its first fragment)
+                // (the wave's issue priority is raised while it issues
+                // products and lowered while it issues loads and waits, so
+                // the SIMD's other wave gets the issue slots it needs for
+                // its products first)
+                __builtin_amdgcn_s_setprio(1);
                 mfma_frag(a_cur, 0, std::integral_constant<int, 0>{}, fr[0], as);
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(0);
                 after_first();
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
                 mfma_frag(a_cur, 0, std::integral_constant<int, 1>{}, fr[0], as);
                 mfma_frag(a_cur, 0, std::integral_constant<int, 2>{}, fr[0], as);
             } else if (32 * j < nvalid) {
@@ -455,6 +462,7 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
             load_act(i + 1);
             load_a(i + 2, a_ring[(r + 2) % 3]);
         });
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (decltype(tail)::value)
             wait_vm_all();
         else
