@@ -28,7 +28,8 @@ workloads run again with bf16 expert weights (moe_expert_mlp_bf16, the
 comparison path the pages name) with their weight-byte and time ratios to
 the MXFP4 runs, and through moe_layer_decode (routing fused into the gate/up
 weight stream) as `fused_decode`; and `probes`: the
-achievable HBM read rate and matrix-core rates measured on this GPU.
+achievable HBM read rate (also in the decode kernels' access order) and
+matrix-core rates measured on this GPU.
 """
 
 from __future__ import annotations
@@ -413,8 +414,10 @@ def quantize_timing(mats, steps, moe, torch) -> dict:
 
 def probes(torch, dev) -> dict:
     """Achievable ceilings on this GPU (libmoe_probe.so): one streaming read of
-    a 4 GiB buffer (far beyond the 256 MB last-level cache), and 8 independent
-    32x32 matrix-core chains per wavefront for each operand type."""
+    a 4 GiB buffer (far beyond the 256 MB last-level cache), the decode
+    kernels' byte counts read in a private range per wavefront and as a
+    grid-wide sweep, and 8 independent 32x32 matrix-core chains per wavefront
+    for each operand type."""
     import ctypes
 
     from mxfp4_quantized_mixture_amd import build as B
@@ -445,6 +448,40 @@ def probes(torch, dev) -> dict:
         torch.cuda.synchronize()
         res["hbm_read_GBs_%d_blocks" % blocks] = 5 * nbytes / (start.elapsed_time(stop) * 1e-3) / 1e9
     del buf
+    # About the decode streaming kernels' byte counts (142, 283 and 508 MB),
+    # read by 2048 wavefronts in two orders: each wavefront a private
+    # contiguous range (as a wavefront owning whole weight tiles reads), and
+    # the grid sweeping the buffer together.  Buffers rotate over more than
+    # 1.5 GB so that no repeat finds its bytes in the 256 MB last-level cache;
+    # the median of 20 single launches, each between two events.
+    L.moe_probe_read_grouped.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    blocks = 256
+    sink = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+    rows = []
+    for cpw in (68, 135, 242):
+        nbytes = blocks * 8 * cpw * 1024
+        nbuf = max(3, (1536 << 20) // nbytes + 1)
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        row = {"bytes": nbytes}
+        for name, group in (("private", 1), ("sweep", blocks * 8)):
+            for b in bufs:
+                assert L.moe_probe_read_grouped(b.data_ptr(), cpw, blocks, group,
+                                                sink.data_ptr(), stream) == 0
+            times = []
+            for r in range(20):
+                start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                start.record()
+                L.moe_probe_read_grouped(bufs[r % nbuf].data_ptr(), cpw, blocks, group,
+                                         sink.data_ptr(), stream)
+                stop.record()
+                torch.cuda.synchronize()
+                times.append(start.elapsed_time(stop))
+            times.sort()
+            row[name + "_us"] = times[len(times) // 2] * 1e3
+            row[name + "_GBs"] = nbytes / (times[len(times) // 2] * 1e-3) / 1e9
+        rows.append(row)
+        del bufs
+    res["read_patterns_2048_waves"] = rows
     names = {0: "fp4_fp4", 1: "fp4_fp6", 2: "fp4_fp8", 3: "fp8_fp8", 4: "f16", 5: "bf16"}
     blocks, iters = 2048, 500
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
@@ -481,7 +518,7 @@ def main() -> int:
                     help="only time mxfp4_quantize (nearest-even and stochastic rounding) on the "
                          "workload's expert weights (W13 and W2)")
     ap.add_argument("--probes", action="store_true",
-                    help="only run the achievable-peak probes (HBM read, matrix cores)")
+                    help="only run the achievable-peak probes (HBM reads, matrix cores)")
     ap.add_argument("--fused-decode", action="store_true",
                     help="only run the workload through moe_layer_decode (routing fused into "
                          "the gate/up weight stream; decode-sized workloads)")

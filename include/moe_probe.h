@@ -49,6 +49,20 @@ MOE_PROBE_API int moe_probe_read(const void *buf, size_t bytes, int blocks, uint
                    hipStream_t stream);
 
 /*
+ * moe_probe_read_grouped -- read blocks * 8 * chunks_per_wave KiB of buf
+ * (16-byte aligned) once with `blocks` blocks of 8 wavefronts, each wavefront
+ * reading chunks_per_wave 1 KiB chunks (16 bytes per lane, four independent
+ * loads per trip).  Groups of `group` consecutive wavefronts interleave their
+ * chunks (chunk c of member r of group q is chunk (q * chunks_per_wave + c) *
+ * group + r of buf): group 1 gives every wavefront a private contiguous range,
+ * group = blocks * 8 makes the grid sweep buf together.  group must divide
+ * blocks * 8 (else 1, nothing enqueued).  Each thread writes the XOR of what it
+ * read to sink[blocks * 512] (uint32).
+ */
+MOE_PROBE_API int moe_probe_read_grouped(const void *buf, int chunks_per_wave, int blocks,
+                                         int group, uint32_t *sink, hipStream_t stream);
+
+/*
  * moe_probe_mfma -- `blocks` blocks of 4 wavefronts, each wavefront issuing
  * iters x 8 independent products of `kind`; each thread writes a sum of its
  * accumulators to sink[blocks * 256] (float).  Total flops =

@@ -32,6 +32,31 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ p
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// The same bytes read in two orders, to separate the cost of the access
+// pattern from that of the bytes: every wavefront (8 per block) reads cpw
+// 1 KiB chunks (64 lanes x 16 B), four independent loads per trip.  The
+// wavefronts form groups of `group` consecutive ones that interleave their
+// chunks: chunk c of member r of group q is chunk (q cpw + c) group + r of the
+// buffer.  group = 1: each wavefront streams a private contiguous range (as a
+// wavefront that owns whole weight tiles does); group = all wavefronts: the
+// grid sweeps the buffer together.  Every index is below nw cpw 64 (nw =
+// gridDim.x * 8, group divides nw; checked by the host).
+__global__ __launch_bounds__(512) void read_grouped_kernel(const u32x4_t* __restrict__ p, int cpw,
+                                                           int group, uint32_t* __restrict__ sink) {
+    const int lane = (int)threadIdx.x & 63;
+    const size_t w = (size_t)blockIdx.x * 8 + (threadIdx.x >> 6);
+    const size_t q = w / (size_t)group, r = w % (size_t)group;
+    auto at = [&](int c) { return p[((q * cpw + c) * group + r) * 64 + lane]; };
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    int c = 0;
+    for (; c + 4 <= cpw; c += 4) {
+        const u32x4_t a = at(c), b = at(c + 1), d = at(c + 2), e = at(c + 3);
+        acc ^= a ^ b ^ d ^ e;
+    }
+    for (; c < cpw; ++c) acc ^= at(c);
+    sink[w * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 // 8 independent accumulator chains per wave, `iters` trips.  The operands
 // are arbitrary register contents (the rate does not depend on values).
 template <int KIND>
@@ -81,6 +106,16 @@ int moe_probe_read(const void* buf, size_t bytes, int blocks, uint32_t* sink, hi
         return 1;
     hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const u32x4_t*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int moe_probe_read_grouped(const void* buf, int chunks_per_wave, int blocks, int group,
+                          uint32_t* sink, hipStream_t stream) {
+    if (!buf || !sink || blocks < 1 || chunks_per_wave < 1 || group < 1 ||
+        (reinterpret_cast<uintptr_t>(buf) & 15u) || ((int64_t)blocks * 8) % group != 0)
+        return 1;
+    hipLaunchKernelGGL(read_grouped_kernel, dim3((unsigned)blocks), dim3(512), 0, stream,
+                       static_cast<const u32x4_t*>(buf), chunks_per_wave, group, sink);
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -57,7 +57,8 @@ def test_probe_library_exports_its_header():
     from mxfp4_quantized_mixture_amd import build as B
     text = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
     declared = set(re.findall(r"MOE_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
-    assert declared == {"moe_probe_read", "moe_probe_mfma", "moe_probe_mfma_flops"}
+    assert declared == {"moe_probe_read", "moe_probe_read_grouped", "moe_probe_mfma",
+                        "moe_probe_mfma_flops"}
     out = os.popen("nm -D --defined-only %s" % B.PROBE_LIB).read()
     assert {l.split()[-1] for l in out.splitlines() if " T " in l} == declared
     P = ctypes.CDLL(B.PROBE_LIB)
@@ -70,6 +71,12 @@ def test_probe_library_exports_its_header():
     assert P.moe_probe_read(None, 1 << 20, 8, FAKE, None) == 1        # bad arguments
     assert P.moe_probe_read(FAKE + 4, 1 << 20, 8, FAKE, None) == 1    # misaligned
     assert P.moe_probe_mfma(9, 8, 1, FAKE, None) == 4                 # unknown kind
+    P.moe_probe_read_grouped.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.moe_probe_read_grouped(None, 4, 8, 1, FAKE, None) == 1      # bad arguments
+    assert P.moe_probe_read_grouped(FAKE + 4, 4, 8, 1, FAKE, None) == 1  # misaligned
+    assert P.moe_probe_read_grouped(FAKE, 4, 8, 3, FAKE, None) == 1      # 3 does not divide 64
+    assert P.moe_probe_read_grouped(FAKE, 0, 8, 1, FAKE, None) == 1      # no chunks
 
 
 def test_status_strings(L):
