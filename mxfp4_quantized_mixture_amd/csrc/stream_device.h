@@ -146,9 +146,16 @@ __device__ void stage_split(const void* __restrict__ src, const int32_t* __restr
             scales[(ss * NT + t) * 64 + gq * 16 + m] = (uint8_t)(se + 127);
         }
     };
-    u32x4_t first[kRaw];
-    const int task0 = threadIdx.x;
+    // The loads of the first two rounds of (row, block) tasks are issued
+    // before anything else: a round loaded after the caller's weight prefetch
+    // would wait for all of it (more than blockDim.x / nblk rows, e.g. 6 or
+    // more rows at K = 2880).  Later rounds (12 or more rows at K = 2880) are
+    // loaded and converted one after the other.
+    u32x4_t first[kRaw], second[kRaw];
+    const int task0 = threadIdx.x, task1 = task0 + (int)blockDim.x;
     load_task(task0 < ntask ? task0 : ntask - 1, first);   // unconditional: see after_loads
+    if (ntask > (int)blockDim.x)                            // uniform in the block
+        load_task(task1 < ntask ? task1 : ntask - 1, second);
     // keeps the caller's loads behind these (and in this loop iteration)
     asm volatile("" ::: "memory");
     // No wavefront issues weight loads before every wavefront has issued its
@@ -177,7 +184,8 @@ __device__ void stage_split(const void* __restrict__ src, const int32_t* __restr
     }
     if (task0 < ntask) convert_task(task0, first);
     after_convert();
-    for (int task = task0 + blockDim.x; task < ntask; task += blockDim.x) {
+    if (task1 < ntask) convert_task(task1, second);
+    for (int task = task1 + blockDim.x; task < ntask; task += blockDim.x) {
         u32x4_t raw[kRaw];
         load_task(task, raw);
         convert_task(task, raw);
