@@ -16,3 +16,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    from tests import report
+
+    if report.LINES:
+        terminalreporter.section("full-size parity")
+        for line in report.LINES:
+            terminalreporter.write_line(line)
