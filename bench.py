@@ -90,12 +90,21 @@ def uses_grouped_gemm(cfg, algo: str) -> bool:
     return algo == "gemm" or (algo == "auto" and cfg.T * cfg.k >= 32 * cfg.E)
 
 
+def kernel_source_digest(source: str) -> str:
+    """sha256 over a kernel's source file followed by every device header of
+    the library (sorted by name): the code a kernel is built from."""
+    csrc = os.path.join(ROOT, "mxfp4_quantized_mixture_amd", "csrc")
+    h = hashlib.sha256()
+    for name in [source] + sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
 def read_traffic(kernel: str, workload: str, source: str, layout: str):
     """HBM bytes per dispatch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source with the same weight layout (else
-    None)."""
+    was taken on the current kernel source (kernel_source_digest) with the same
+    weight layout (else None)."""
     path = os.path.join(ROOT, "profiles", "%s.%s.traffic.txt" % (kernel, workload))
-    src = os.path.join(ROOT, "mxfp4_quantized_mixture_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -103,7 +112,7 @@ def read_traffic(kernel: str, workload: str, source: str, layout: str):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = kernel_source_digest(source)
     if fields.get("kernel_source_sha256") != digest or fields.get("weight_layout") != layout:
         return None
     try:
