@@ -63,6 +63,10 @@ __device__ __forceinline__ int row_rot(int r) { return (r >> 3) & 1; }
 // gate/up epilogue: h of the block's 128 pairs x 128 features in fp32, rows
 // of kHRow floats
 constexpr int kHRow = 132;
+// down epilogue: each wave's 128 pairs x 64 outputs of fp16 y, rows of
+// kYPitch bytes (128 + 16: 16-byte aligned rows, at most 2-way bank
+// conflicts for the 8-byte writes)
+constexpr int kYPitch = 144;
 
 // Direct global -> LDS load of 16 bytes per lane: lane l's 16 bytes at
 // base + voff land at LDS byte lds_base + 16 l (lds_base wave-uniform).
@@ -537,31 +541,67 @@ __global__ __launch_bounds__(64 * WR, 8 / WR) void expert_gemm_kernel(
         // and no y overflows or underflows whatever its range.  Lane (n, g) holds
         // 16 of the fragment's 32 outputs of pair 32 j + n, lane (n, 1 - g) the
         // other 16.
+        //
+        // The wave's 128 pairs x 64 outputs go through LDS first (rows of
+        // kYPitch bytes, free once every wave is past its last step), so that
+        // each global store instruction writes 8 whole 128-byte rows instead of
+        // 16 bytes in each of 32 rows (measured: the direct stores took about a
+        // tenth of the kernel).
+        __syncthreads();                                // every wave is done with the stage buffers
+        uint8_t* ytile = lds + (size_t)wave * kGemmRows * kYPitch;
+        int sc[NA][NB];
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-            if (a >= wcnt) break;
-            const int f = wf0 + a;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 float m = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(acc[a][j][i]));
                 m = fmaxf(m, __shfl_xor(m, 32));
-                const int s = y_scale_exponent(m);
+                const int sj = y_scale_exponent(m);
+                sc[a][j] = sj;
+                // element i: output 32 a + 8 (i / 4) + 4 g + i % 4 of the wave's 64,
+                // pair 32 j + n
+                uint8_t* trow = ytile + (32 * j + n) * kYPitch + 2 * (32 * a + 4 * g);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t h2[2];
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        h2[c] = f32_to_f16_bits(__builtin_ldexpf(acc[a][j][4 * w + 2 * c], -sj)) |
+                                (f32_to_f16_bits(__builtin_ldexpf(acc[a][j][4 * w + 2 * c + 1], -sj)) << 16);
+                    *reinterpret_cast<u32x2_t*>(trow + 16 * w) = u32x2_t{h2[0], h2[1]};
+                }
+            }
+        }
+        // (a wave reads back only what it wrote: LDS operations of one wave
+        // complete in order, and the compiler waits for the writes' data)
+        // scale bytes: f = wf0 and wf0 + 1 are adjacent (wf0 even) in the row
+        // of NOUT / 32 bytes (even: NOUT % 64 == 0)
+        if (g == 0 && wcnt > 0) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
                 const int r = 32 * j + n;
                 if (r < nvalid) {
-                    // element i: output 32 f + 8 (i / 4) + 4 g + i % 4 of pair r
-                    uint16_t* orow = y16 + (size_t)(row0 + r) * NOUT + 32 * f + 4 * g;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        uint32_t h2[2];
-#pragma unroll
-                        for (int c = 0; c < 2; ++c)
-                            h2[c] = f32_to_f16_bits(__builtin_ldexpf(acc[a][j][4 * w + 2 * c], -s)) |
-                                    (f32_to_f16_bits(__builtin_ldexpf(acc[a][j][4 * w + 2 * c + 1], -s)) << 16);
-                        *reinterpret_cast<u32x2_t*>(orow + 8 * w) = u32x2_t{h2[0], h2[1]};
-                    }
-                    if (g == 0) ys[(size_t)(row0 + r) * (NOUT / 32) + f] = (uint8_t)(s + 127);
+                    uint8_t* srow = ys + (size_t)(row0 + r) * (NOUT / 32) + wf0;
+                    if (wcnt == 2)
+                        *reinterpret_cast<uint16_t*>(srow) =
+                            (uint16_t)((sc[0][j] + 127) | ((sc[1][j] + 127) << 8));
+                    else
+                        srow[0] = (uint8_t)(sc[0][j] + 127);
+                }
+            }
+        }
+        // lane l: 16 bytes (outputs 8 (l % 8) .. + 7 of the wave's 64) of
+        // pair 8 q + l / 8
+        const int cq = lane & 7;
+        if (8 * cq < 32 * wcnt) {
+#pragma unroll 4
+            for (int q = 0; q < kGemmRows / 8; ++q) {
+                const int r = 8 * q + (lane >> 3);
+                if (r < nvalid) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ytile + r * kYPitch + 16 * cq);
+                    *reinterpret_cast<u32x4_t*>(y16 + (size_t)(row0 + r) * NOUT + 32 * wf0 + 8 * cq) = v;
                 }
             }
         }
@@ -599,12 +639,13 @@ constexpr int kDownWaves = 4;
 
 // Dynamic LDS of expert_gemm_kernel: two step buffers of activation chunks,
 // the weight scales of the block's 2 WR A fragments (K bytes each), 8 KiB of
-// dummy destinations for the staging; gate/up also needs room for its
-// epilogue's fp32 h tile.
+// dummy destinations for the staging; the epilogues reuse it (gate/up for its
+// fp32 h tile, down for its waves' fp16 y tiles) and need at least that much.
 size_t gemm_lds_bytes(int K, bool gate_up) {
     const int wr = gate_up ? kGateUpWaves : kDownWaves;
     size_t b = (size_t)2 * kGemmRows * kStepPitch + (size_t)2 * wr * K + 8 * 1024;
     if (gate_up) b = std::max(b, (size_t)kGemmRows * kHRow * sizeof(float));
+    else b = std::max(b, (size_t)wr * kGemmRows * kYPitch);
     return b;
 }
 
