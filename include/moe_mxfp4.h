@@ -260,6 +260,9 @@ MOE_API moe_status_t moe_route(const uint16_t *x, const float *wr, const float *
  *    E4M3 terms (relative error below 2^-12 within those 13 binades);
  *  - grouped GEMM: x and h each as 3 E2M3 (fp6) terms (error below 2^-12 of
  *    the block's largest magnitude); h goes from fp32 straight to its terms;
+ *    each pair's down output y is held as fp16 with one power-of-two scale
+ *    per 32 outputs that brings their largest magnitude into [2^14, 2^15)
+ *    (error below 2^-11 of it, no range limit);
  * fp32 accumulation and combine; output rounded to bf16 (nearest even).
  * Preconditions: as moe_route, plus 32 <= F, F % 32 == 0, a shape one of the
  * algorithms takes (see moe_mlp_algo_t), the routing arrays consistent with
@@ -362,8 +365,9 @@ MOE_API moe_status_t moe_expert_mlp_bf16_ex(const uint16_t *x, const uint16_t *w
  *                      leaves them so.  Calls that overlap on one workspace
  *                      race.
  * Preconditions: as moe_route and moe_expert_mlp, plus T <= 64,
- * T * E <= 8192 and a shape the streaming kernels take (D <= 3840,
- * F <= 2944 for packed codes; D, F <= 4096).
+ * T * E <= 8192 and a shape the streaming kernels take (D <= 3840 and
+ * F <= 2944, their LDS budget; with packed codes also D % 64 == 0 and
+ * F % 64 == 0).
  * Device-side waits are bounded: if one gives up (a launch whose blocks
  * could not all make progress), the call's outputs are invalid, an error is
  * recorded in the control block (read with moe_layer_decode_error), all
