@@ -204,9 +204,10 @@ def check_route(x, wr, b, k, what):
 
 
 ROUTE_CASES = ([("tiny", s) for s in range(10)] +
-               [("gptoss20b_decode", s) for s in range(3)] +
-               [("gptoss120b_decode", s) for s in range(3)] +
-               [("gptoss20b_prefill", 0), ("gptoss120b_prefill_skewed", 0)])
+               [("gptoss20b_decode", s) for s in range(10)] +
+               [("gptoss120b_decode", s) for s in range(10)] +
+               [("gptoss20b_prefill", s) for s in range(3)] +
+               [("gptoss120b_prefill_skewed", s) for s in range(3)])
 
 
 @pytest.mark.parametrize("name,seed", ROUTE_CASES)
@@ -387,7 +388,7 @@ def check_layer(inp, tokens="all", what="", algo=moe.MLP_AUTO, packed=False):
     return out
 
 
-@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("seed", range(10))
 def test_layer_tiny(seed):
     check_layer(Inputs(MI.CONFIGS["tiny"], seed), what="tiny/seed%d" % seed)
 
@@ -396,14 +397,19 @@ def test_layer_tiny(seed):
 # compare every 16th token plus the first and last row of every 128-pair
 # tile of every expert (so the tile table, the work remap across the XCDs
 # and the 32-bit offsets are exercised at their real counts).
-@pytest.mark.parametrize("name,tokens", [("gptoss20b_decode", "all"),
-                                         ("gptoss120b_decode", "all"),
-                                         ("gptoss20b_prefill", "tiles"),
-                                         ("gptoss120b_prefill_skewed", "tiles")])
-def test_layer_workloads(name, tokens):
+# Seeds: 0-9 for the decode shapes, 0-2 for the prefill shapes.
+LAYER_CASES = ([("gptoss20b_decode", "all", s) for s in range(10)] +
+               [("gptoss120b_decode", "all", s) for s in range(10)] +
+               [("gptoss20b_prefill", "tiles", s) for s in range(3)] +
+               [("gptoss120b_prefill_skewed", "tiles", s) for s in range(3)])
+
+
+@pytest.mark.parametrize("name,tokens,seed", LAYER_CASES)
+def test_layer_workloads(name, tokens, seed):
     # in the weight layout the benchmark uses: packed wherever the kernels take it
     cfg = MI.CONFIGS[name]
-    check_layer(Inputs(cfg, 0), tokens=tokens, what=name, packed=packed_ok(cfg))
+    check_layer(Inputs(cfg, seed), tokens=tokens, what="%s/seed%d" % (name, seed),
+                packed=packed_ok(cfg))
 
 
 EDGE = [
