@@ -173,12 +173,17 @@ MlpPlan plan_mlp(int T, int D, int F, int E, int k) {
     return p;
 }
 
-// Blocks per expert for the streaming kernels: about 256 blocks in all (one
-// per CU of MI355X, so every block runs in the first round) and at least 2
-// per expert, so untouched experts' CUs are reused by the dispatcher; at
-// least 8 tiles (one per wavefront) per block where possible.
+// Blocks per expert for the streaming kernels: about 224 blocks in all (7/8
+// of MI355X's 256 CUs, one block per CU, so every block runs in the first
+// round) and at least 2 per expert, so untouched experts' CUs are reused by
+// the dispatcher; at least 8 tiles (one per wavefront) per block where
+// possible.  The weight stream is bound by HBM, not by the CUs streaming it:
+// at the 20B decode shape (32 experts) 7 blocks per expert measured 57.1 +
+// 36.9 us for gate/up and down against 58.7 + 37.2 us with 8 (and 6: 58.3 +
+// 37.7, 5: 56.5 + 40.2, 4: 65.9 + 47.6); the 120B decode shape (128 experts,
+// about 112 touched) keeps 2 per expert, about 224 active blocks.
 static int stream_blocks_per_expert(int E, int ntiles) {
-    int bpe = (256 + E - 1) / E;
+    int bpe = (224 + E - 1) / E;
     if (bpe < 2) bpe = 2;
     if (bpe > ntiles / kStreamWaves) bpe = ntiles / kStreamWaves;
     return bpe < 1 ? 1 : bpe;
