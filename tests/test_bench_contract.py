@@ -47,3 +47,26 @@ def test_decode_work_matches_the_mxfp4_byte_count():
     wp = b.algorithmic_work(p, np.full(p.E, 1024))
     assert wp["gateup_flops"] == 4 * 2880 * 2880 * 8192 * 4
     assert wp["step_flops"] == 6 * 2880 * 2880 * 8192 * 4
+
+
+def test_traffic_summaries_are_used_only_on_the_sources_they_were_taken_on(tmp_path):
+    # read_traffic accepts a committed counter summary only while its digest
+    # covers the current kernel file and every device header: a change to a
+    # shared header (where the kernel bodies live) makes it report null.
+    import shutil
+    b = _bench_module()
+    root = tmp_path / "repo"
+    shutil.copytree(os.path.join(ROOT, "mxfp4_quantized_mixture_amd", "csrc"),
+                    root / "mxfp4_quantized_mixture_amd" / "csrc")
+    (root / "profiles").mkdir()
+    b.ROOT = str(root)
+    digest = b.kernel_source_digest("expert_mlp.hip")
+    (root / "profiles" / "gateup.w.traffic.txt").write_text(
+        "# test summary\nkernel: k\nworkload: w\nweight_layout: packed\n"
+        "kernel_source_sha256: %s\nhbm_bytes_per_dispatch: 1234\n" % digest)
+    assert b.read_traffic("gateup", "w", "expert_mlp.hip", "packed") == 1234.0
+    assert b.read_traffic("gateup", "w", "expert_mlp.hip", "row-major") is None
+    hdr = root / "mxfp4_quantized_mixture_amd" / "csrc" / "stream_device.h"
+    hdr.write_text(hdr.read_text() + "\n// changed\n")
+    assert b.kernel_source_digest("expert_mlp.hip") != digest
+    assert b.read_traffic("gateup", "w", "expert_mlp.hip", "packed") is None
