@@ -21,7 +21,12 @@ namespace moe {
 // ---------------------------------------------------------------------------
 
 constexpr int kStreamWaves = 8;
-constexpr int kMaxWaveTiles = 4;       // tile outputs a wavefront holds in registers
+// tile outputs a wavefront holds in registers until its last load: 8 in the
+// streaming kernels (255-256 VGPRs), 6 in the fused decode front (its other
+// state would make 8 spill).  Measured at the 120B decode shape (11-12 tiles
+// per wavefront): 296.1 us per step with 8 and 297.6 with 6 against 300.3 with 4.
+template <bool kFused>
+constexpr int kMaxWaveTiles = kFused ? 6 : 8;
 
 // Staged activations.  The weights enter the matrix cores exactly as stored
 // (E2M1 codes + E8M0 block scales, v_mfma_scale_f32_16x16x128_f8f6f4 with an
@@ -406,13 +411,14 @@ __device__ __forceinline__ void expert_stream_body(
         lds_barrier();                         // not __syncthreads: the weight loads stay in flight
 
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc_gate = {0.f, 0.f, 0.f, 0.f};
-        // The first kMaxWaveTiles tile results stay in registers until the
+        // The first kMaxWaveTiles<kFused> tile results stay in registers until the
         // wave has issued its last load: on gfx9 the vector memory counter
         // also covers stores, so an early store makes later load waits wait
         // for its write too (measured: 1.5 us per launch at 3 tiles per
         // wave).  Further tiles (many tiles per wave, when blocks per expert
         // are few) are stored as soon as they are computed.
-        f32x4_t obuf[kMaxWaveTiles];
+        constexpr int kTilesHeld = kMaxWaveTiles<kFused>;
+        f32x4_t obuf[kTilesHeld];
         const int ostride = kGateUp ? F : D;
         auto epilogue = [&](int s) {
             const int j = s / seg;
@@ -423,9 +429,9 @@ __device__ __forceinline__ void expert_stream_body(
             } else {
                 res = acc;
             }
-            if (j < kMaxWaveTiles) {
+            if (j < kTilesHeld) {
 #pragma unroll
-                for (int jj = 0; jj < kMaxWaveTiles; ++jj)
+                for (int jj = 0; jj < kTilesHeld; ++jj)
                     if (jj == j) obuf[jj] = res;
             } else if (m < nvalid) {
                 const int tile = a + wave + j * kStreamWaves;
@@ -464,7 +470,7 @@ __device__ __forceinline__ void expert_stream_body(
         }
         if (m < nvalid) {
 #pragma unroll
-            for (int jj = 0; jj < kMaxWaveTiles; ++jj) {
+            for (int jj = 0; jj < kTilesHeld; ++jj) {
                 if (jj < my_tiles) {
                     const int tile = a + wave + jj * kStreamWaves;
                     *reinterpret_cast<f32x4_t*>(out + (size_t)(row0 + m) * ostride + tile * 16 + 4 * g) =
