@@ -451,6 +451,34 @@ def test_layer_grouped_gemm_shapes(cfg):
     check_layer(Inputs(cfg, 4), what=cfg.name + "/grouped-gemm", algo=moe.MLP_GROUPED_GEMM)
 
 
+def _random_shapes(n, seed):
+    """Seeded random small layers that both expert algorithms take: D and F
+    multiples of 64 (so every column range, wave and fragment count of the
+    grouped GEMM occurs: D / 32 and F / 32 from 2 to 24), T from 1 to 700
+    (short and many tiles), E up to 48, k up to min(E, 8); every fourth with
+    the Zipf-like router bias (skewed expert loads)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 49))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        out.append(MI.MoEConfig("random%d" % i, T=int(rng.integers(1, 701)),
+                                D=64 * int(rng.integers(1, 13)), F=64 * int(rng.integers(1, 13)),
+                                E=E, k=k, bias="zipf" if i % 4 == 3 else "zero"))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(32, 2024)
+
+
+@pytest.mark.parametrize("cfg", RANDOM_SHAPES,
+                         ids=["%s_T%d_D%d_F%d_E%d_k%d" % (c.name, c.T, c.D, c.F, c.E, c.k)
+                              for c in RANDOM_SHAPES])
+@pytest.mark.parametrize("algo", [moe.MLP_GROUPED_GEMM, moe.MLP_STREAM])
+def test_layer_random_shapes(cfg, algo):
+    check_layer(Inputs(cfg, 11), what="%s/algo %d" % (cfg.name, algo), algo=algo)
+
+
 class W2ScaledInputs(Inputs):
     """Inputs whose W2 blocks are multiplied by powers of two (exact in
     bf16): "spread" draws a factor 2^(30 - r), r in [0, 40], per 32-element
