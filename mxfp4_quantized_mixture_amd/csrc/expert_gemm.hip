@@ -109,11 +109,10 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // Tile table: expert e's pairs [offsets[e], offsets[e+1]) in tiles of
 // kGemmRows, experts in order.  tiles[2 i] = first sorted row of tile i,
 // tiles[2 i + 1] = e | rows << 16; tiles[2 max_tiles] = number of tiles.
-// Computed by one block of 256 threads (E <= 256).
+// Computed by one block of 256 threads (E <= 256), with 256 ints of LDS at part.
 // ---------------------------------------------------------------------------
 __device__ void gemm_tile_table(const int32_t* __restrict__ offsets, int E, int max_tiles,
-                                int32_t* __restrict__ tiles) {
-    __shared__ int part[256];
+                                int32_t* __restrict__ tiles, int* part) {
     const int e = threadIdx.x;
     const int beg = e < E ? offsets[e] : 0;
     const int ne = e < E ? offsets[e + 1] - beg : 0;
@@ -136,29 +135,65 @@ __device__ void gemm_tile_table(const int32_t* __restrict__ offsets, int E, int 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 rows -> fp6 term rows, one thread per (row, 64-element step); the
+// bf16 rows -> fp6 term rows, one thread per (row, 64-element step) item; the
 // grid's extra first block computes the tile table (one launch fewer; as the
 // first block dispatched it runs beside the conversion, not after it).
+//
+// Rows are contiguous (K % 64 == 0), so item i reads the 128 bytes at 128 i
+// of src and writes the 160 bytes at 160 i of tq: a wavefront's 64 items are
+// one contiguous 8 KiB range in and one 10 KiB range out.  A whole wavefront
+// moves them with whole-line accesses (lane l: 16 bytes at 16 l + 1024 c) and
+// regroups them by item through its own LDS area: items at a pitch of 144
+// bytes going in (the 16-byte accesses of 16 lanes at 16 different items hit
+// 16 different groups of 4 banks), 160 going out (at most 2 lanes per group;
+// the area of 10 KiB per wavefront lets four blocks share a CU).  The wavefront at
+// the end of the range, with fewer than 64 items, moves each item by itself.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void split_terms_kernel(const uint16_t* __restrict__ src,
-                                                          int rows, int K,
-                                                          uint8_t* __restrict__ tq,
-                                                          const int32_t* __restrict__ offsets,
-                                                          int E, int max_tiles,
-                                                          int32_t* __restrict__ tiles) {
+constexpr int kSplitInPitch = 144;
+constexpr int kSplitOutPitch = kTermStep;
+constexpr int kSplitWaves = 4;
+constexpr int kSplitWaveLds = 64 * kSplitOutPitch;   // the in and out layouts share it
+static_assert(64 * kSplitInPitch <= kSplitWaveLds && kSplitWaveLds % 16 == 0, "split LDS");
+
+__global__ __launch_bounds__(64 * kSplitWaves) void split_terms_kernel(
+    const uint16_t* __restrict__ src, int rows, int K, uint8_t* __restrict__ tq,
+    const int32_t* __restrict__ offsets, int E, int max_tiles, int32_t* __restrict__ tiles) {
+    __shared__ __align__(16) uint8_t lds[kSplitWaves * kSplitWaveLds];
     if (blockIdx.x == 0) {
-        gemm_tile_table(offsets, E, max_tiles, tiles);
+        gemm_tile_table(offsets, E, max_tiles, tiles, reinterpret_cast<int*>(lds));
         return;
     }
     const int S = K / 64;
-    const int64_t idx = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)rows * S) return;
-    const int row = (int)(idx / S), s = (int)(idx - (int64_t)row * S);
-    const uint16_t* p = src + (size_t)row * K + (size_t)s * 64;
+    const int64_t n = (int64_t)rows * S;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t i0 = ((int64_t)(blockIdx.x - 1) * kSplitWaves + wave) * 64;
+    if (i0 >= n) return;
+    const int64_t idx = i0 + lane;
+    const bool whole = i0 + 64 <= n;                  // uniform in the wavefront
+    uint8_t* wl = lds + wave * kSplitWaveLds;
+    const uint8_t* in = reinterpret_cast<const uint8_t*>(src);
     // the whole 128-byte step is loaded before any of it is converted
     u32x4_t raw[8];
+    if (whole) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) raw[c] = *reinterpret_cast<const u32x4_t*>(p + c * 8);
+        for (int c = 0; c < 8; ++c)
+            raw[c] = *reinterpret_cast<const u32x4_t*>(in + (size_t)i0 * 128 + 1024 * c + 16 * lane);
+        // unit lane % 8 of item 8 c + lane / 8
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            *reinterpret_cast<u32x4_t*>(wl + (8 * c + (lane >> 3)) * kSplitInPitch + 16 * (lane & 7)) =
+                raw[c];
+        // (a wavefront reads back only what it wrote: LDS operations of one
+        // wavefront complete in order)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            raw[c] = *reinterpret_cast<const u32x4_t*>(wl + lane * kSplitInPitch + 16 * c);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            raw[c] = idx < n ? *reinterpret_cast<const u32x4_t*>(in + (size_t)idx * 128 + 16 * c)
+                             : u32x4_t{0u, 0u, 0u, 0u};
+    }
     __builtin_amdgcn_sched_barrier(0);
     float v[64];
 #pragma unroll
@@ -170,11 +205,29 @@ __global__ __launch_bounds__(256) void split_terms_kernel(const uint16_t* __rest
         }
     uint32_t out[kTermStep / 4];
     fp6_encode_step(v, out);
-    uint8_t* o = tq + ((size_t)row * S + s) * kTermStep;
+    if (whole) {
+        // (every lane's reads of the area above returned before the
+        // conversion, which used them, so its own item may overwrite it)
 #pragma unroll
-    for (int w = 0; w < kTermStep / 16; ++w)
-        *reinterpret_cast<u32x4_t*>(o + 16 * w) =
-            u32x4_t{out[4 * w], out[4 * w + 1], out[4 * w + 2], out[4 * w + 3]};
+        for (int w = 0; w < kTermStep / 16; ++w)
+            *reinterpret_cast<u32x4_t*>(wl + lane * kSplitOutPitch + 16 * w) =
+                u32x4_t{out[4 * w], out[4 * w + 1], out[4 * w + 2], out[4 * w + 3]};
+        // (at pitch 160 the area holds the range as it is stored: 16-byte
+        // unit u = 64 c + lane is at 16 u in both)
+        static_assert(kSplitOutPitch == kTermStep, "the area is the stored range");
+        uint8_t* o = tq + (size_t)i0 * kTermStep;
+#pragma unroll
+        for (int c = 0; c < kTermStep / 16; ++c) {
+            const int u = 64 * c + lane;
+            *reinterpret_cast<u32x4_t*>(o + 16 * u) = *reinterpret_cast<const u32x4_t*>(wl + 16 * u);
+        }
+    } else if (idx < n) {
+        uint8_t* o = tq + (size_t)idx * kTermStep;
+#pragma unroll
+        for (int w = 0; w < kTermStep / 16; ++w)
+            *reinterpret_cast<u32x4_t*>(o + 16 * w) =
+                u32x4_t{out[4 * w], out[4 * w + 1], out[4 * w + 2], out[4 * w + 3]};
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -697,7 +750,10 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
     uint8_t* hq = reinterpret_cast<uint8_t*>(base + p.off_h);
     int32_t* tiles = reinterpret_cast<int32_t*>(base + p.off_tiles);
     const int64_t nsplit = (int64_t)p.T * (p.D / 64);
-    hipLaunchKernelGGL(split_terms_kernel, dim3((unsigned)((nsplit + 255) / 256 + 1)), dim3(256), 0,
+    constexpr int kSplitThreads = 64 * kSplitWaves;
+    hipLaunchKernelGGL(split_terms_kernel,
+                       dim3((unsigned)((nsplit + kSplitThreads - 1) / kSplitThreads + 1)),
+                       dim3(kSplitThreads), 0,
                        stream, x, p.T, p.D, xq, offsets, p.E, p.max_tiles, tiles);
     if (events) {
         const hipError_t er = hipEventRecord(events[0], stream);
