@@ -247,7 +247,7 @@ hipError_t launch_decode(const DecodePlan& p, bool packed, const uint16_t* x, co
     const float* h = reinterpret_cast<const float*>(base + p.off_mlp + p.mlp.off_h);
     er = launch_stream_down(p.mlp, packed, h, w2q, w2s, offsets, sorted, y, stream);
     if (er != hipSuccess) return er;
-    return launch_combine_rows(p.mlp.T, p.mlp.D, p.mlp.k, y, w, pos, out, events, stream);
+    return launch_combine_slots(p.mlp.T, p.mlp.D, p.mlp.k, y, w, out, events, stream);
 }
 
 }  // namespace moe

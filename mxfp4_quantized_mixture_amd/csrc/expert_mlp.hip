@@ -77,6 +77,41 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
 }
 
+// The same combine over y stored in slot order (row t k + j holds the pair
+// of slot j of token t, as the streaming down kernel writes it): every
+// address is known at once, so a thread waits for one memory round trip.
+__global__ __launch_bounds__(256) void combine_slots_kernel(
+    const float* __restrict__ y, const float* __restrict__ topk_w, int T, int D, int k,
+    uint16_t* __restrict__ out) {
+    const int q = D / 4;
+    const int64_t n = (int64_t)T * q;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int t = (int)(i / q), d4 = (int)(i % q);
+        float wv[kCombineMaxK];
+        f32x4_t v[kCombineMaxK];
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+                wv[j] = topk_w[t * k + j];
+                v[j] = *reinterpret_cast<const f32x4_t*>(y + (size_t)(t * k + j) * D + d4 * 4);
+            }
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j < k) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = __builtin_fmaf(wv[j], v[j][c], acc[c]);
+            }
+        }
+        uint2 o;
+        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(out + (size_t)t * D + d4 * 4) = o;
+    }
+}
+
 // The same combine over y stored in fp16 with a power-of-two scale per
 // (pair, 32-output fragment) (ys byte = s + 127, value = y16 2^s), as the
 // grouped GEMM's down kernel writes it: eight outputs per thread (16-byte
@@ -189,9 +224,6 @@ static int stream_blocks_per_expert(int E, int ntiles) {
     return bpe < 1 ? 1 : bpe;
 }
 
-static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
-                                 const int32_t* pos, uint16_t* out, hipEvent_t* events,
-                                 hipStream_t stream);
 static hipError_t launch_combine16(const MlpPlan& p, const uint16_t* y16, const uint8_t* ys,
                                    const float* topk_w, const int32_t* pos, uint16_t* out,
                                    hipEvent_t* events, hipStream_t stream);
@@ -256,13 +288,7 @@ hipError_t launch_mlp(const MlpPlan& p, int algo, bool packed, const uint16_t* x
     er = packed ? launch_stream<false, true>(p, h, w2q, w2s, offsets, sorted, y, stream)
                 : launch_stream<false, false>(p, h, w2q, w2s, offsets, sorted, y, stream);
     if (er != hipSuccess) return er;
-    return launch_combine(p, y, topk_w, pos, out, events, stream);
-}
-
-static hipError_t launch_combine(const MlpPlan& p, const float* y, const float* topk_w,
-                                 const int32_t* pos, uint16_t* out, hipEvent_t* events,
-                                 hipStream_t stream) {
-    return launch_combine_rows(p.T, p.D, p.k, y, topk_w, pos, out, events, stream);
+    return launch_combine_slots(p.T, p.D, p.k, y, topk_w, out, events, stream);
 }
 
 static hipError_t launch_combine16(const MlpPlan& p, const uint16_t* y16, const uint8_t* ys,
@@ -295,6 +321,24 @@ hipError_t launch_combine_rows(int T, int D, int k, const float* y, const float*
     int64_t gb = (n + 255) / 256;
     if (gb > 8192) gb = 8192;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)gb), dim3(256), 0, stream, y, topk_w, pos,
+                       T, D, k, out);
+    if (events) {
+        const hipError_t er = hipEventRecord(events[3], stream);
+        if (er != hipSuccess) return er;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_slots(int T, int D, int k, const float* y, const float* topk_w,
+                                uint16_t* out, hipEvent_t* events, hipStream_t stream) {
+    if (events) {
+        const hipError_t er = hipEventRecord(events[2], stream);
+        if (er != hipSuccess) return er;
+    }
+    const int64_t n = (int64_t)T * (D / 4);
+    int64_t gb = (n + 255) / 256;
+    if (gb > 8192) gb = 8192;
+    hipLaunchKernelGGL(combine_slots_kernel, dim3((unsigned)gb), dim3(256), 0, stream, y, topk_w,
                        T, D, k, out);
     if (events) {
         const hipError_t er = hipEventRecord(events[3], stream);

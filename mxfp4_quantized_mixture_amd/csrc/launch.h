@@ -30,7 +30,7 @@ hipError_t launch_route(const RoutePlan& p, const uint16_t* x, const float* wr, 
                         int32_t* sorted, int32_t* pos, float* logits_out, void* ws,
                         hipStream_t stream);
 
-// Workspace of moe_expert_mlp: y (fp32 [P, D] for weight streaming; fp16
+// Workspace of moe_expert_mlp: y (fp32 [P, D] in slot order for weight streaming; fp16
 // [P, D] plus a scale byte per 32 outputs for the grouped GEMM), h (fp32 [P, F]
 // for weight streaming, fp6 term rows for the grouped GEMM: one region),
 // then the grouped GEMM's x term rows and tile table.
@@ -70,8 +70,9 @@ hipError_t launch_mlp_gemm(const MlpPlan& p, bool packed, const uint16_t* x, con
                            uint8_t* ys, char* base,
                            hipEvent_t* events, hipStream_t stream);
 
-// the streaming down kernel alone (h fp32 [P, F] -> y fp32 [P, D]), and the
-// streaming gate/up kernel's blocks per expert (expert_mlp.hip)
+// the streaming down kernel alone (h fp32 [P, F] in pair order -> y fp32
+// [P, D] in slot order: the pair of slot j of token t at row t k + j), and
+// the streaming gate/up kernel's blocks per expert (expert_mlp.hip)
 hipError_t launch_stream_down(const MlpPlan& p, bool packed, const float* h, const uint8_t* w2q,
                               const uint8_t* w2s, const int32_t* offsets, const int32_t* sorted,
                               float* y, hipStream_t stream);
@@ -82,6 +83,10 @@ int stream_blocks_gate_up(const MlpPlan& p);
 hipError_t launch_combine_rows(int T, int D, int k, const float* y, const float* topk_w,
                                const int32_t* pos, uint16_t* out, hipEvent_t* events,
                                hipStream_t stream);
+// out[t] = bf16(sum_j topk_w[t, j] y[t k + j]), slots in order, over y in
+// slot order (expert_mlp.hip); events as above
+hipError_t launch_combine_slots(int T, int D, int k, const float* y, const float* topk_w,
+                                uint16_t* out, hipEvent_t* events, hipStream_t stream);
 
 // bf16-weight comparison path (expert_bf16.hip): workspace = y fp32 [P, D]
 // then h fp32 [P, F]

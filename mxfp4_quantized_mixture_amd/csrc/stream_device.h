@@ -298,7 +298,8 @@ __device__ __forceinline__ void compute_batch(const WBatch<NB>& B, int ss0, int 
 
 // kGateUp: A = [gate rows; up rows] of W13 (NS = 2), B = x rows (2 fp8 terms),
 //          epilogue h = silu(g) * u -> fp32.
-// else:    A = W2 rows (NS = 1), B = h rows (3 fp8 terms), epilogue y -> fp32.
+// else:    A = W2 rows (NS = 1), B = h rows (3 fp8 terms), epilogue y -> fp32
+//          (row t k + j for the pair of slot j of token t).
 //
 // A wavefront streams one weight row range at a time: for each of its tiles
 // the gate rows over the whole contraction, then the up rows (the gate sums
@@ -400,6 +401,14 @@ __device__ __forceinline__ void expert_stream_body(
         const int row0 = row_beg + tg;
         const int nvalid = min(16, ne - tg);
         if (tg > 0) __syncthreads();           // previous group's rows no longer read
+        // Output row of this lane's pair: h in pair (sorted) order, the rows
+        // the down kernel reads contiguously; y in slot order (pair p of
+        // slot sorted[p] = t k + j at row t k + j), so that the combine finds a
+        // token's k rows without the permutation.  (Issued ahead of the group's
+        // activation and weight loads, so it is back before any of them is
+        // waited for.)
+        int orow = row0 + m;
+        if constexpr (!kGateUp) orow = sorted[row0 + (m < nvalid ? m : nvalid - 1)];
         // the weight prefetch goes out right behind the first activation loads
         // (fused: the first group's first batch went out before the routing
         // wait, the rest of its ring follows the first conversion as usual)
@@ -435,7 +444,7 @@ __device__ __forceinline__ void expert_stream_body(
                     if (jj == j) obuf[jj] = res;
             } else if (m < nvalid) {
                 const int tile = a + wave + j * kStreamWaves;
-                *reinterpret_cast<f32x4_t*>(out + (size_t)(row0 + m) * ostride + tile * 16 + 4 * g) = res;
+                *reinterpret_cast<f32x4_t*>(out + (size_t)orow * ostride + tile * 16 + 4 * g) = res;
             }
         };
         auto consume = [&](const WBatch<NB>& W, int s) {
@@ -473,7 +482,7 @@ __device__ __forceinline__ void expert_stream_body(
             for (int jj = 0; jj < kTilesHeld; ++jj) {
                 if (jj < my_tiles) {
                     const int tile = a + wave + jj * kStreamWaves;
-                    *reinterpret_cast<f32x4_t*>(out + (size_t)(row0 + m) * ostride + tile * 16 + 4 * g) =
+                    *reinterpret_cast<f32x4_t*>(out + (size_t)orow * ostride + tile * 16 + 4 * g) =
                         obuf[jj];
                 }
             }
